@@ -1,0 +1,155 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library: block quantization,
+ * dequantization, the W4A4 block-scaled GEMM of the DiT linears and the
+ * NVFP4 KV cache.
+ *
+ * Where the operations come from.  LongLive-2.0 ("An NVFP4 Parallel
+ * Infrastructure for Long Video Generation"): the arXiv abstract page
+ * (fugumt.com, Abstract) states that inference on Blackwell runs W4A4 NVFP4
+ * and that the KV cache is quantized into NVFP4 to save memory; the
+ * d9249.github.io review (section "Core idea / structure / operation") adds
+ * that a parallel dequantization kernel restores the NVFP4 KV cache; the
+ * yourai.pro news page lists faster FP4 dequantization and reduced KV-cache
+ * synchronization among the NVFP4 inference-path optimizations.  The pages
+ * fix no numeric detail; the format below is the NVFP4 layout (E2M1 element
+ * codes, one E4M3 scale per 16 elements, one fp32 per-tensor scale) with
+ * OCP Microscaling v1.0 / OCP FP8 E4M3FN bit encodings.
+ *
+ * Format (one tensor of `rows` x `k`, k contiguous, k % 16 == 0):
+ *   s_g            fp32, = RN_f32(amax / (6 * 448)), amax = max |x| over the
+ *                  tensor (over each head for the KV cache);
+ *   scales[r][j]   u8 E4M3FN, = RNE_SAT(amax of elements 16j..16j+15 of row r
+ *                  / (6 * s_g)); 0 for an all-zero block or s_g == 0;
+ *   codes[r][i]    u8, two E2M1 codes: element 2i in bits 3:0, element 2i+1
+ *                  in bits 7:4; code = sign bit (bit 3) | RNE_SAT(|x| /
+ *                  (val(scale) * s_g)) on {0, .5, 1, 1.5, 2, 3, 4, 6};
+ *   dequantized    RN_out(val(code) * val(scale) * s_g), one rounding.
+ * Every rounding is one round-to-nearest-even of the exact real value (ties
+ * to the even code / byte / significand); results are bit-exact and
+ * independent of launch configuration.
+ *
+ * Conventions for every call:
+ *   - pointers are device pointers (HBM) owned by the caller; the library
+ *     allocates nothing and keeps no state between calls;
+ *   - `stream` is a hipStream_t passed as void* (NULL = null stream); every
+ *     call only enqueues work on it and never synchronizes the host;
+ *   - arguments are validated before anything is enqueued: on any error
+ *     status nothing was launched and no output was touched;
+ *   - NVFP4_ERR_LAUNCH reports a failed kernel launch (for example no GPU);
+ *     device faults surface at the caller's next synchronization;
+ *   - inputs must be finite; NaN/Inf inputs give unspecified outputs;
+ *   - data pointers must be 16-byte aligned, scale/s_g pointers 4-byte
+ *     aligned (NVFP4_ERR_ALIGN otherwise);
+ *   - calls on one stream are ordered; calls on different streams that
+ *     share an output buffer race.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,   /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,  /* a size is negative, zero where not allowed, not a multiple of 16 along k, or too large */
+  NVFP4_ERR_ALIGN = 3,  /* a pointer is not aligned as required */
+  NVFP4_ERR_DTYPE = 4,  /* unknown dtype */
+  NVFP4_ERR_LAUNCH = 5, /* the HIP runtime rejected a launch */
+  NVFP4_ERR_FLAGS = 6   /* unknown flags value */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
+
+#define NVFP4_SCALE_COMPUTE 0 /* compute s_g from the data and write it to *s_g */
+#define NVFP4_SCALE_GIVEN 1   /* use the s_g already stored at *s_g (device) */
+
+/* Version of this ABI (NVFP4_ABI_VERSION). */
+int nvfp4_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *nvfp4_status_string(int status);
+
+/*
+ * Quantize x [rows][k] (dtype F32 or BF16, row-major) to NVFP4.
+ *   codes   [rows][k/2]  u8 out      scales [rows][k/16] u8 out
+ *   s_g     [1] fp32: out with NVFP4_SCALE_COMPUTE, in with NVFP4_SCALE_GIVEN
+ * Per the arXiv abstract (W4A4 NVFP4 inference: weights and activations
+ * quantized).  rows == 0 is allowed (COMPUTE then writes s_g = 0).  With
+ * COMPUTE the call runs three kernels (amax partials, s_g finalize, encode);
+ * the codes buffer serves as scratch for the amax partials before it is
+ * overwritten.  Requires k > 0, k % 16 == 0, rows * k < 2^40.
+ */
+nvfp4_status_t nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                              uint8_t *scales, float *s_g, int flags, void *stream);
+
+/*
+ * Dequantize: y[r][i] = RN_ydtype(val(code) * val(scale) * s_g), y [rows][k]
+ * of dtype F32 or BF16 (one rounding of the exact product).  Same shape
+ * rules as nvfp4_quantize.  Per the d9249.github.io review (dequantization
+ * kernel restoring NVFP4 data) and the yourai.pro page (faster FP4
+ * dequantization).
+ */
+nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *s_g,
+                                int64_t rows, int64_t k, void *y, int y_dtype, void *stream);
+
+/*
+ * W4A4 GEMM, the nn.Linear convention C = A . B^T:
+ *   A [M][K] as (a_codes [M][K/2], a_scales [M][K/16], a_sg [1])
+ *   B [N][K] as (b_codes [N][K/2], b_scales [N][K/16], b_sg [1])
+ *   C [M][N] row-major, dtype F32 or BF16:
+ *   C[m][n] = RN_cdtype(a_sg * b_sg * sum_k val(qA)val(sA) * val(qB)val(sB))
+ * Each decoded element val(q)*val(s) is exact in fp16; products are summed
+ * by fp16 MFMA in fp32 (order unspecified, deterministic), then scaled.
+ * Per the arXiv abstract and the landx blog (section on NVFP4: GEMMs on
+ * 4-bit weights and activations).  Requires M, N > 0, K > 0, K % 16 == 0,
+ * M, N < 2^31.
+ */
+nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sg,
+                          const uint8_t *b_codes, const uint8_t *b_scales, const float *b_sg,
+                          int64_t M, int64_t N, int64_t K, void *c, int c_dtype, void *stream);
+
+/*
+ * Activation-quantizing linear: quantize A (a_dtype F32 or BF16, [M][K])
+ * with a per-tensor scale computed from the data, then C = A_q . B^T as in
+ * nvfp4_gemm.  a_sg [1], a_codes [M][K/2] and a_scales [M][K/16] are outputs
+ * owned by the caller (the packed activation, bit-identical to
+ * nvfp4_quantize's); the GEMM reads them back from L2/MALL.  One call
+ * enqueues amax, finalize, encode and GEMM kernels on `stream`.
+ */
+nvfp4_status_t nvfp4_gemm_fused_act(const void *a, int a_dtype, int64_t M, int64_t K, float *a_sg,
+                                    uint8_t *a_codes, uint8_t *a_scales, const uint8_t *b_codes,
+                                    const uint8_t *b_scales, const float *b_sg, int64_t N, void *c,
+                                    int c_dtype, void *stream);
+
+/*
+ * NVFP4 KV cache quantize: kv [heads][tokens][head_dim] bf16 ->
+ *   codes [heads][tokens][head_dim/2], scales [heads][tokens][head_dim/16],
+ *   head_scales [heads] fp32 (one s_g per head, from that head's amax).
+ * Blocks of 16 run along head_dim.  Per the arXiv abstract (KV cache
+ * quantized into NVFP4) and the d9249.github.io review (Table 3: NVFP4 KV
+ * cache lowers peak memory).  Requires heads > 0, tokens >= 0,
+ * head_dim % 16 == 0.
+ */
+nvfp4_status_t kv_quantize(const void *kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                           uint8_t *codes, uint8_t *scales, float *head_scales, void *stream);
+
+/*
+ * NVFP4 KV cache dequantize to bf16 [heads][tokens][head_dim]:
+ *   out = RN_bf16(val(code) * val(scale) * head_scales[h]).
+ * The "parallel dequantization" of the d9249.github.io review (section
+ * "Core idea / structure / operation").
+ */
+nvfp4_status_t kv_dequantize(const uint8_t *codes, const uint8_t *scales, const float *head_scales,
+                             int64_t heads, int64_t tokens, int64_t head_dim, void *kv_out,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H_ */

@@ -1,0 +1,223 @@
+"""NVFP4 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, exact CPU reference (``nvfp4_oracle.c``, built with gcc) for
+the NVFP4 quantizer, dequantizer, W4A4 GEMM and NVFP4 KV cache.  Only the
+test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the product library never does, and the two share
+no code.  The numeric contract it implements is stated at the top of
+``nvfp4_oracle.c`` (E2M1 codes, one E4M3 scale per 16 elements, fp32
+per-tensor scale amax/(6*448), every rounding one round-to-nearest-even of the
+exact value).  The pages on LongLive-2.0 (arXiv abstract page, Abstract;
+d9249.github.io review, "Core idea / structure / operation") name W4A4 NVFP4
+linears and an NVFP4 KV cache but fix no numeric detail.
+
+Arrays are numpy: float32 arrays are fp32 tensors, uint16 arrays are bf16
+bit patterns.  Every function pinned by the tests in ``tests/test_oracle_*``.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force=False):
+    """Compile nvfp4_oracle.c into liboracle.so (gcc, -O2, no fp contraction)."""
+    if (not force and os.path.exists(_LIB_PATH)
+            and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC)):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    c_i64, c_p, c_f, c_d, c_i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double, ctypes.c_int
+    sig = {
+        "orc_version": (c_i, []),
+        "orc_num_threads": (c_i, []),
+        "orc_e2m1_value": (c_d, [c_i]),
+        "orc_e4m3_value": (c_d, [c_i]),
+        "orc_global_scale": (c_f, [c_f]),
+        "orc_block_scale": (c_i, [c_d, c_f]),
+        "orc_e2m1_code": (c_i, [c_d, c_d]),
+        "orc_round_bf16": (ctypes.c_uint16, [c_d]),
+        "orc_amax": (c_i, [c_p, c_i, c_i64, c_p]),
+        "orc_quantize_with_scale": (c_i, [c_p, c_i, c_i64, c_i64, c_f, c_p, c_p]),
+        "orc_quantize": (c_i, [c_p, c_i, c_i64, c_i64, c_p, c_p, c_p]),
+        "orc_dequantize": (c_i, [c_p, c_p, c_f, c_i64, c_i64, c_p, c_i]),
+        "orc_gemm_ref": (c_i, [c_p, c_p, c_f, c_p, c_p, c_f, c_i64, c_i64, c_i64,
+                               c_p, c_i64, c_p, c_i64, c_p, c_p]),
+        "orc_kv_quantize": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
+        "orc_kv_dequantize": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i64, c_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _check(status):
+    if status == -1:
+        raise OracleError("non-finite input")
+    if status != 0:
+        raise OracleError("bad shape (status %d)" % status)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(x):
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 arrays or uint16 bf16 bit patterns, got %s" % x.dtype)
+
+
+def num_threads():
+    return _load().orc_num_threads()
+
+
+# ---- scalar format functions -------------------------------------------
+
+def e2m1_value(code):
+    return _load().orc_e2m1_value(int(code))
+
+
+def e4m3_value(byte):
+    return _load().orc_e4m3_value(int(byte))
+
+
+def global_scale(amax):
+    """s_g = RN_f32(amax / 2688) as np.float32."""
+    return np.float32(_load().orc_global_scale(float(np.float32(amax))))
+
+
+def block_scale(amax_b, s_g):
+    """E4M3 byte of RNE_SAT(amax_b / (6 s_g))."""
+    return _load().orc_block_scale(float(amax_b), float(np.float32(s_g)))
+
+
+def e2m1_code(x, S):
+    """sign | RNE_SAT_E2M1(|x| / S); S = val(s_b) * s_g given exactly."""
+    return _load().orc_e2m1_code(float(x), float(S))
+
+
+def round_bf16(v):
+    """bf16 bit pattern of RN_bf16(v) for an exact fp64 value v."""
+    return int(_load().orc_round_bf16(float(v)))
+
+
+# ---- tensors -------------------------------------------------------------
+
+def amax(x):
+    x = np.ascontiguousarray(x)
+    out = ctypes.c_float(0.0)
+    _check(_load().orc_amax(_ptr(x), _dtype_of(x), x.size, ctypes.byref(out)))
+    return np.float32(out.value)
+
+
+def quantize(x, s_g=None):
+    """x [rows, k] -> (codes uint8 [rows, k/2], scales uint8 [rows, k/16], s_g float32)."""
+    x = np.ascontiguousarray(x)
+    if x.ndim != 2:
+        raise OracleError("quantize expects a 2-D array")
+    rows, k = x.shape
+    codes = np.zeros((rows, k // 2), np.uint8)
+    scales = np.zeros((rows, k // 16), np.uint8)
+    lib = _load()
+    if s_g is None:
+        sg = ctypes.c_float(0.0)
+        _check(lib.orc_quantize(_ptr(x), _dtype_of(x), rows, k, _ptr(codes), _ptr(scales), ctypes.byref(sg)))
+        return codes, scales, np.float32(sg.value)
+    _check(lib.orc_quantize_with_scale(_ptr(x), _dtype_of(x), rows, k, float(np.float32(s_g)),
+                                       _ptr(codes), _ptr(scales)))
+    return codes, scales, np.float32(s_g)
+
+
+def dequantize(codes, scales, s_g, out="bf16"):
+    """-> bf16 bit patterns (uint16) or float32 [rows, k]."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    if out == "bf16":
+        y = np.zeros((rows, k), np.uint16)
+        dt = BF16
+    elif out == "f32":
+        y = np.zeros((rows, k), np.float32)
+        dt = F32
+    else:
+        raise ValueError(out)
+    _check(_load().orc_dequantize(_ptr(codes), _ptr(scales), float(np.float32(s_g)), rows, k, _ptr(y), dt))
+    return y
+
+
+def gemm_ref(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, rows=None, cols=None):
+    """Reference of C = A . B^T in fp64 and sum_k |a_k b_k| for the selected rows/cols.
+
+    Returns (ref, abssum), float64 arrays [len(rows), len(cols)].
+    """
+    a_codes = np.ascontiguousarray(a_codes, np.uint8)
+    a_scales = np.ascontiguousarray(a_scales, np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, np.uint8)
+    b_scales = np.ascontiguousarray(b_scales, np.uint8)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != K:
+        raise OracleError("K mismatch")
+    r = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    ref = np.zeros((nr, nc), np.float64)
+    tot = np.zeros((nr, nc), np.float64)
+    _check(_load().orc_gemm_ref(_ptr(a_codes), _ptr(a_scales), float(np.float32(a_sg)),
+                                _ptr(b_codes), _ptr(b_scales), float(np.float32(b_sg)), M, N, K,
+                                None if r is None else _ptr(r), nr, None if c is None else _ptr(c), nc,
+                                _ptr(ref), _ptr(tot)))
+    return ref, tot
+
+
+def kv_quantize(kv):
+    """kv bf16 bits uint16 [H, T, D] -> (codes [H,T,D/2], scales [H,T,D/16], head_scales [H])."""
+    kv = np.ascontiguousarray(kv)
+    if kv.dtype != np.uint16 or kv.ndim != 3:
+        raise OracleError("kv_quantize expects uint16 bf16 bits [H, T, D]")
+    H, T, D = kv.shape
+    codes = np.zeros((H, T, D // 2), np.uint8)
+    scales = np.zeros((H, T, D // 16), np.uint8)
+    hs = np.zeros(H, np.float32)
+    _check(_load().orc_kv_quantize(_ptr(kv), H, T, D, _ptr(codes), _ptr(scales), _ptr(hs)))
+    return codes, scales, hs
+
+
+def kv_dequantize(codes, scales, head_scales):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    hs = np.ascontiguousarray(head_scales, np.float32)
+    H, T, D = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+    out = np.zeros((H, T, D), np.uint16)
+    _check(_load().orc_kv_dequantize(_ptr(codes), _ptr(scales), _ptr(hs), H, T, D, _ptr(out)))
+    return out

@@ -1,0 +1,330 @@
+/*
+ * NVFP4 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, exact reference for what the GPU library computes.  Only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * load it; the product path never does.  It shares no code, header or table
+ * with the HIP library.
+ *
+ * What it follows.  The pages (LongLive-2.0: "An NVFP4 Parallel Infrastructure
+ * for Long Video Generation", arXiv abstract page, Abstract; d9249.github.io
+ * review, section "Core idea / structure / operation") say the DiT linears run
+ * W4A4 NVFP4 and that the KV cache is stored as NVFP4 and restored by a
+ * dequantization kernel, but they define no numeric detail.  The numeric
+ * contract used here is:
+ *   - E2M1 element codes on the grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} (with sign),
+ *     OCP Microscaling v1.0 bit layout: bit 3 sign, bits 2:1 exponent (bias 1),
+ *     bit 0 mantissa; element 2i in the low nibble of byte i.
+ *   - one E4M3 scale byte (OCP FP8 E4M3FN: bias 7, max 448 = 0x7E, 0x7F NaN)
+ *     per 16 contiguous elements along the reduction axis;
+ *   - one fp32 per-tensor (per-head for the KV cache) scale
+ *     s_g = RN_f32(amax / (6 * 448));
+ *   - block scale s_b = RNE_SAT_E4M3(amax_block / (6 * s_g));
+ *   - code q = RNE_SAT_E2M1(x / (val(s_b) * s_g)), sign always kept;
+ *   - dequantized value = RN_out(val(q) * val(s_b) * s_g).
+ * Every rounding is ONE round-to-nearest-even of the exact real value, with
+ * ties going to the even code / even byte / even significand.  Every decision
+ * below is taken by comparing the input with an exactly representable
+ * boundary (a midpoint times the scale, exact in fp64), so no division
+ * rounding enters any decision.
+ *
+ * All entry points return 0 on success and a negative value on a non-finite
+ * input or a bad shape.  Arrays are host memory, row-major, reduction axis
+ * contiguous.  OpenMP runs over rows.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_OK 0
+#define ORC_ERR_NONFINITE (-1)
+#define ORC_ERR_SHAPE (-2)
+
+int orc_version(void) { return 1; }
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---- scalar formats -------------------------------------------------- */
+
+/* bf16 bit pattern -> its exact value. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double load_elem(const void *x, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float *)x)[i];
+  return bf16_to_double(((const uint16_t *)x)[i]);
+}
+
+/* E2M1 nibble -> value.  Magnitude 2^(e-1) * (1 + m/2) for e >= 1 and
+ * m/2 for e == 0; bit 3 is the sign (0x8 is -0.0). */
+double orc_e2m1_value(int code) {
+  int e = (code >> 1) & 3, m = code & 1;
+  double mag = e ? ldexp(1.0 + m / 2.0, e - 1) : m / 2.0;
+  return (code & 8) ? -mag : mag;
+}
+
+/* E4M3FN byte -> value.  2^(e-7) * (1 + m/8) for e >= 1, 2^-6 * m/8 for
+ * e == 0; exponent 15 with mantissa 7 is NaN (no infinities). */
+double orc_e4m3_value(int byte) {
+  int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return s ? -mag : mag;
+}
+
+/* s_g = RN_f32(amax / 2688): the float nearest to the exact quotient, ties to
+ * the even significand.  The fp64 quotient gives a candidate within one fp32
+ * ulp; the exact choice is made among it and its two neighbours by comparing
+ * |f * 2688 - amax|, which is exact in fp64 (f*2688 has at most 29
+ * significant bits and the two terms are within a factor of two). */
+float orc_global_scale(float amax) {
+  if (!(amax > 0.0f)) return 0.0f;
+  float c = (float)((double)amax / 2688.0);
+  float cand[3] = {nextafterf(c, 0.0f), c, nextafterf(c, INFINITY)};
+  float best = cand[0];
+  double best_err = INFINITY;
+  for (int i = 0; i < 3; i++) {
+    double err = fabs((double)cand[i] * 2688.0 - (double)amax);
+    uint32_t bits;
+    memcpy(&bits, &cand[i], 4);
+    if (err < best_err || (err == best_err && (bits & 1u) == 0)) {
+      best = cand[i];
+      best_err = err;
+    }
+  }
+  return best;
+}
+
+/* Block scale byte: RNE_SAT_E4M3(amax_b / (6 s_g)).  The ratio is placed
+ * among the 127 finite non-negative E4M3 values by comparing amax_b with
+ * midpoint(b-1, b) * 6 * s_g, exact in fp64 (<= 5 + 2 + 24 significant
+ * bits).  At a midpoint the even byte wins; anything above the last
+ * midpoint (432) saturates to 0x7E = 448; a zero s_g or zero block gives 0. */
+int orc_block_scale(double amax_b, float s_g) {
+  if (s_g == 0.0f || amax_b == 0.0) return 0;
+  double den = 6.0 * (double)s_g;
+  int best = 0;
+  for (int b = 1; b < 127; b++) {
+    double mid = 0.5 * (orc_e4m3_value(b - 1) + orc_e4m3_value(b)) * den;
+    if (amax_b > mid || (amax_b == mid && (b % 2) == 0)) best = b;
+  }
+  return best;
+}
+
+/* Element code: sign(x) | RNE_SAT_E2M1(|x| / S) with S = val(s_b) * s_g
+ * (exact in fp64).  |x| is compared with midpoint(i-1, i) * S, exact in
+ * fp64 (<= 3 + 4 + 24 significant bits); ties take the even code; above
+ * 5 S everything saturates to 6 (code 7).  S == 0 keeps only the sign. */
+int orc_e2m1_code(double x, double S) {
+  int sign = signbit(x) ? 8 : 0;
+  if (S == 0.0) return sign;
+  double a = fabs(x);
+  int best = 0;
+  for (int i = 1; i < 8; i++) {
+    double mid = 0.5 * (orc_e2m1_value(i - 1) + orc_e2m1_value(i)) * S;
+    if (a > mid || (a == mid && (i % 2) == 0)) best = i;
+  }
+  return sign | best;
+}
+
+/* One round-to-nearest-even of an exact fp64 value to bfloat16 (8
+ * significant bits, fp32 exponent range, subnormal step 2^-133).  Returns the
+ * bf16 bit pattern. */
+uint16_t orc_round_bf16(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  uint16_t sign = neg ? 0x8000 : 0;
+  if (a == 0.0) return sign;
+  int E;
+  frexp(a, &E); /* a = f * 2^E, f in [0.5, 1): leading bit has weight 2^(E-1) */
+  int ulp_exp = E - 8;
+  if (ulp_exp < -133) ulp_exp = -133;
+  double q = ldexp(a, -ulp_exp); /* exact: power-of-two scaling */
+  double qf = floor(q);
+  double frac = q - qf;
+  if (frac > 0.5 || (frac == 0.5 && fmod(qf, 2.0) != 0.0)) qf += 1.0;
+  double r = ldexp(qf, ulp_exp);
+  if (r >= ldexp(1.0, 128)) return sign | 0x7f80; /* overflow to infinity */
+  float rf = (float)r; /* exact: r is a bf16 value */
+  uint32_t u;
+  memcpy(&u, &rf, 4);
+  return sign | (uint16_t)((u >> 16) & 0x7fff);
+}
+
+/* ---- tensors --------------------------------------------------------- */
+
+/* amax = max |x| over n elements (exact). */
+int orc_amax(const void *x, int dtype, int64_t n, float *amax) {
+  double m = 0.0;
+  for (int64_t i = 0; i < n; i++) {
+    double v = load_elem(x, dtype, i);
+    if (!isfinite(v)) return ORC_ERR_NONFINITE;
+    if (fabs(v) > m) m = fabs(v);
+  }
+  *amax = (float)m; /* exact: m is an input value */
+  return ORC_OK;
+}
+
+/* Quantize rows x k elements with a given s_g into codes [rows][k/2] and
+ * scale bytes [rows][k/16]. */
+int orc_quantize_with_scale(const void *x, int dtype, int64_t rows, int64_t k, float s_g,
+                            uint8_t *codes, uint8_t *scales) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t blk = 0; blk < k / 16; blk++) {
+      double v[16];
+      double amax_b = 0.0;
+      for (int i = 0; i < 16; i++) {
+        v[i] = load_elem(x, dtype, r * k + blk * 16 + i);
+        if (!isfinite(v[i])) bad = 1;
+        if (fabs(v[i]) > amax_b) amax_b = fabs(v[i]);
+      }
+      int sb = orc_block_scale(amax_b, s_g);
+      double S = orc_e4m3_value(sb) * (double)s_g; /* exact */
+      scales[r * (k / 16) + blk] = (uint8_t)sb;
+      for (int i = 0; i < 16; i += 2) {
+        int lo = orc_e2m1_code(v[i], S), hi = orc_e2m1_code(v[i + 1], S);
+        codes[r * (k / 2) + blk * 8 + i / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+  return bad ? ORC_ERR_NONFINITE : ORC_OK;
+}
+
+/* Full per-tensor quantization: amax -> s_g -> blocks. */
+int orc_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+                 uint8_t *scales, float *s_g) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
+  float amax;
+  int st = orc_amax(x, dtype, rows * k, &amax);
+  if (st) return st;
+  *s_g = orc_global_scale(amax);
+  return orc_quantize_with_scale(x, dtype, rows, k, *s_g, codes, scales);
+}
+
+/* y = RN_out(val(q) * val(s_b) * s_g); the product is exact in fp64
+ * (<= 2 + 4 + 24 significant bits) and rounded once. */
+int orc_dequantize(const uint8_t *codes, const uint8_t *scales, float s_g, int64_t rows, int64_t k,
+                   void *y, int y_dtype) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t i = 0; i < k; i++) {
+      int byte = codes[r * (k / 2) + i / 2];
+      int q = (i & 1) ? (byte >> 4) : (byte & 15);
+      double v = orc_e2m1_value(q) * orc_e4m3_value(scales[r * (k / 16) + i / 16]) * (double)s_g;
+      if (y_dtype == ORC_F32)
+        ((float *)y)[r * k + i] = (float)v; /* one RNE of the exact value */
+      else
+        ((uint16_t *)y)[r * k + i] = orc_round_bf16(v);
+    }
+  }
+  return ORC_OK;
+}
+
+/* Exact decoded row without s_g: d[i] = val(q_i) * val(s_b(i)) (<= 6 bits). */
+static void decode_row(const uint8_t *codes, const uint8_t *scales, int64_t k, int64_t r, double *d) {
+  for (int64_t i = 0; i < k; i++) {
+    int byte = codes[r * (k / 2) + i / 2];
+    int q = (i & 1) ? (byte >> 4) : (byte & 15);
+    d[i] = orc_e2m1_value(q) * orc_e4m3_value(scales[r * (k / 16) + i / 16]);
+  }
+}
+
+/* GEMM reference for C = A . B^T with A [M][K], B [N][K] in NVFP4:
+ *   ref[i][j] = s_gA s_gB sum_k a_k b_k,  abssum[i][j] = s_gA s_gB sum_k |a_k b_k|
+ * over the selected rows (row_idx, n_rows; NULL = all M) and columns (col_idx,
+ * n_cols; NULL = all N).  Each a_k b_k is exact in fp64 (<= 12 bits); the sum
+ * runs in fp64 in k order, the relative error is below K * 2^-53. */
+int orc_gemm_ref(const uint8_t *a_codes, const uint8_t *a_scales, float a_sg, const uint8_t *b_codes,
+                 const uint8_t *b_scales, float b_sg, int64_t M, int64_t N, int64_t K,
+                 const int64_t *row_idx, int64_t n_rows, const int64_t *col_idx, int64_t n_cols,
+                 double *ref, double *abssum) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return ORC_ERR_SHAPE;
+  int64_t nr = row_idx ? n_rows : M, nc = col_idx ? n_cols : N;
+  for (int64_t i = 0; i < nr; i++)
+    if (row_idx && (row_idx[i] < 0 || row_idx[i] >= M)) return ORC_ERR_SHAPE;
+  for (int64_t j = 0; j < nc; j++)
+    if (col_idx && (col_idx[j] < 0 || col_idx[j] >= N)) return ORC_ERR_SHAPE;
+  double gscale = (double)a_sg * (double)b_sg; /* exact: 24 x 24 bits */
+  /* Decode the selected B rows once; each A row is decoded by its thread. */
+  double *bd = (double *)malloc(sizeof(double) * (size_t)(nc * K));
+  if (!bd) return ORC_ERR_SHAPE;
+  for (int64_t j = 0; j < nc; j++) decode_row(b_codes, b_scales, K, col_idx ? col_idx[j] : j, bd + j * K);
+  int fail = 0;
+#pragma omp parallel reduction(| : fail)
+  {
+    double *ad = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!ad) fail = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nr; i++) {
+      if (!ad) continue;
+      decode_row(a_codes, a_scales, K, row_idx ? row_idx[i] : i, ad);
+      for (int64_t j = 0; j < nc; j++) {
+        const double *b = bd + j * K;
+        double s = 0.0, t = 0.0;
+        for (int64_t kk = 0; kk < K; kk++) {
+          double p = ad[kk] * b[kk];
+          s += p;
+          t += fabs(p);
+        }
+        ref[i * nc + j] = s * gscale;
+        abssum[i * nc + j] = t * gscale;
+      }
+    }
+    free(ad);
+  }
+  free(bd);
+  return fail ? ORC_ERR_SHAPE : ORC_OK;
+}
+
+/* ---- NVFP4 KV cache: [heads][tokens][head_dim], one s_g per head ------ */
+
+/* Per head h: s_g[h] = RN_f32(amax over the head's tokens x head_dim / 2688),
+ * then the same 16-element blocks along head_dim as above. */
+int orc_kv_quantize(const uint16_t *kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                    uint8_t *codes, uint8_t *scales, float *head_scales) {
+  if (heads <= 0 || tokens < 0 || head_dim <= 0 || head_dim % 16 != 0) return ORC_ERR_SHAPE;
+  for (int64_t h = 0; h < heads; h++) {
+    const uint16_t *xh = kv + h * tokens * head_dim;
+    float amax;
+    int st = orc_amax(xh, ORC_BF16, tokens * head_dim, &amax);
+    if (st) return st;
+    head_scales[h] = orc_global_scale(amax);
+    st = orc_quantize_with_scale(xh, ORC_BF16, tokens, head_dim, head_scales[h],
+                                 codes + h * tokens * (head_dim / 2),
+                                 scales + h * tokens * (head_dim / 16));
+    if (st) return st;
+  }
+  return ORC_OK;
+}
+
+/* Per head: bf16 = RN_bf16(val(q) * val(s_b) * s_g[h]). */
+int orc_kv_dequantize(const uint8_t *codes, const uint8_t *scales, const float *head_scales,
+                      int64_t heads, int64_t tokens, int64_t head_dim, uint16_t *out) {
+  if (heads <= 0 || tokens < 0 || head_dim <= 0 || head_dim % 16 != 0) return ORC_ERR_SHAPE;
+  for (int64_t h = 0; h < heads; h++) {
+    int st = orc_dequantize(codes + h * tokens * (head_dim / 2), scales + h * tokens * (head_dim / 16),
+                            head_scales[h], tokens, head_dim, out + h * tokens * head_dim, ORC_BF16);
+    if (st) return st;
+  }
+  return ORC_OK;
+}

@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs shaped like a 5B video DiT's linears and KV cache.
+
+This module only draws random tensors; it holds none of the NVFP4 arithmetic,
+so the oracle side (tests) and the GPU side (binding, bench) can both use it.
+The LongLive-2.0 pages (d9249.github.io review, "Evidence" section: the 5B
+model at 1280x720; d9249 "Core idea": multi-shot attention sinks) give no
+tensor shapes; the sizes below are hidden 3072, FFN 14336, 24 heads x 128,
+65,536 cached tokens.
+
+Recipes (every draw is torch.randn/rand in fp32 on the CPU from
+torch.Generator seeded 1000*cfg + t, t = 0 activations/K, 1 weights/V,
+2 auxiliary draws; bf16 tensors are the fp32 draws rounded to nearest even):
+  1  A, B fp32 [256, 256] ~ N(0, 1)
+  2  A bf16 [4096, 3072] ~ N(0, 1), entries with an i.i.d. Bernoulli(0.005)
+     mask scaled x20 (outliers);  W bf16 [3072, 3072] ~ N(0, 0.02)
+  3  A bf16 [16384, 3072] = std_k * N(0, 1), std_k = exp(0.5 z_k), z ~ N(0, 1)
+     per input channel k;  W bf16 [14336, 3072] ~ N(0, 0.02)
+  4  A bf16 [16384, 14336] = GELU(N(0, 1)) (erf form, fp32);
+     W bf16 [3072, 14336] ~ N(0, 0.01)
+  5  K, V bf16 [24, 65536, 128] ~ N(0, 1), tokens 0..3 of every head x8
+     (attention-sink tokens)
+Sizes can be overridden (same recipe) for small parity cases.
+"""
+import torch
+
+CONFIGS = {
+    1: dict(workload="nvfp4_gemm_256_f32", M=256, N=256, K=256, a_dtype="f32", c_dtype="f32"),
+    2: dict(workload="dit_attn_proj_4096x3072x3072", M=4096, N=3072, K=3072, a_dtype="bf16", c_dtype="bf16"),
+    3: dict(workload="dit_ffn_up_fused_16384x14336x3072", M=16384, N=14336, K=3072, a_dtype="bf16",
+            c_dtype="bf16"),
+    4: dict(workload="dit_ffn_down_16384x3072x14336", M=16384, N=3072, K=14336, a_dtype="bf16",
+            c_dtype="bf16"),
+    5: dict(workload="nvfp4_kv_cache_24x65536x128", H=24, T=65536, D=128),
+}
+
+
+def generator(cfg, t):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1000 * cfg + t)
+    return g
+
+
+def activations(cfg, M=None, K=None):
+    """Activation matrix A [M, K] of config cfg (CPU tensor)."""
+    c = CONFIGS[cfg]
+    M = c["M"] if M is None else M
+    K = c["K"] if K is None else K
+    if cfg == 1:
+        return torch.randn(M, K, generator=generator(1, 0), dtype=torch.float32)
+    a = torch.randn(M, K, generator=generator(cfg, 0), dtype=torch.float32)
+    if cfg == 2:
+        mask = torch.rand(M, K, generator=generator(2, 2), dtype=torch.float32) < 0.005
+        a = torch.where(mask, a * 20.0, a)
+    elif cfg == 3:
+        z = torch.randn(K, generator=generator(3, 2), dtype=torch.float32)
+        a = a * torch.exp(0.5 * z)[None, :]
+    elif cfg == 4:
+        a = torch.nn.functional.gelu(a, approximate="none")
+    return a.to(torch.bfloat16)
+
+
+def weights(cfg, N=None, K=None):
+    """Weight matrix W [N, K] of config cfg (CPU tensor)."""
+    c = CONFIGS[cfg]
+    N = c["N"] if N is None else N
+    K = c["K"] if K is None else K
+    w = torch.randn(N, K, generator=generator(cfg, 1), dtype=torch.float32)
+    if cfg == 1:
+        return w
+    std = {2: 0.02, 3: 0.02, 4: 0.01}[cfg]
+    return (w * std).to(torch.bfloat16)
+
+
+def kv_cache(H=None, T=None, D=None, sinks=4):
+    """(K, V) bf16 [H, T, D] of the KV-cache workload (CPU tensors)."""
+    c = CONFIGS[5]
+    H = c["H"] if H is None else H
+    T = c["T"] if T is None else T
+    D = c["D"] if D is None else D
+    out = []
+    for t in (0, 1):
+        x = torch.randn(H, T, D, generator=generator(5, t), dtype=torch.float32)
+        x[:, :sinks, :] *= 8.0
+        out.append(x.to(torch.bfloat16))
+    return tuple(out)
+
+
+def bf16_bits(t):
+    """uint16 numpy view of a bf16 CPU tensor (for the oracle)."""
+    import numpy as np
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
