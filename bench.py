@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step is the DiT FFN up-projection of a long-video chunk as a W4A4 NVFP4
+linear: the bf16 activations A [16384, 3072] are quantized to NVFP4 (amax,
+per-tensor scale, per-16 E4M3 scales and E2M1 codes) and multiplied with the
+pre-quantized weights W [14336, 3072] (C = A . W^T, bf16 out).  The step is
+the same kernel sequence nvfp4_gemm_fused_act enqueues, issued as
+nvfp4_quantize + nvfp4_gemm so that HIP events can bracket the GEMM kernel.
+Weights are quantized once, outside the timed region.  Inputs are seeded
+synthetic tensors (workloads/), resident in HBM before timing starts.
+
+Printed: one JSON line with the step throughput (TFLOP/s = 2 M N K / step
+time), the GEMM kernel's roofline against the fp16/bf16 dense MFMA peak,
+secondary HBM throughputs (activation quantize of the FFN down-projection
+input, NVFP4 KV-cache round trip), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "W4A4 NVFP4 GEMM TFLOP/s (M16384 K3072 N14336) + quant/dequant HBM GB/s"
+MFMA_PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# Whole-pass HBM bytes per element (bf16 data, 4-bit code + one 8-bit scale per 16 elements).
+B_AMAX = 2.0
+B_ENCODE = 2.0 + 0.5 + 1.0 / 16
+B_DEQUANT = 0.5 + 1.0 / 16 + 2.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--no-secondary", action="store_true", help="skip the quantize / KV-cache bandwidth lines")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = events(torch, 2)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the NVFP4 hot path runs on a single MI355X here; "
+              "--gpus %d is not supported (multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import workloads
+    from long_video_dit_amd import nvfp4
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[3]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    flop = 2.0 * M * N * K
+
+    log("generating inputs", M, N, K)
+    a = workloads.activations(3).to(dev)
+    w = workloads.weights(3).to(dev)
+    wq = nvfp4.quantize(w)  # weights: once, outside the timed region
+    del w
+    aq = (torch.empty(M, K // 2, dtype=torch.uint8, device=dev),
+          torch.empty(M, K // 16, dtype=torch.uint8, device=dev),
+          torch.empty(1, dtype=torch.float32, device=dev))
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    gemm_s, gemm_e = events(torch, args.steps), events(torch, args.steps)
+
+    def step(i=None):
+        nvfp4.quantize(a, out=aq[:2], s_g_out=aq[2])
+        if i is not None:
+            gemm_s[i].record()
+        nvfp4.gemm(aq, wq, out=c)
+        if i is not None:
+            gemm_e[i].record()
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing", args.steps, "steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = sum(s.elapsed_time(e) for s, e in zip(gemm_s, gemm_e)) / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (gemm_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "M": M, "N": N, "K": K, "a_dtype": "bf16", "c_dtype": "bf16",
+                   "w_format": "nvfp4", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_w4a4_kernel", "achieved": round(achieved, 1),
+                     "peak": MFMA_PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "gemm_ms": round(gemm_ms, 4)},
+    }
+    log("step %.3f ms, gemm %.3f ms -> %.1f TFLOP/s step, %.1f TFLOP/s gemm" % (ms_per_step, gemm_ms, value,
+                                                                             achieved))
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(torch, nvfp4, workloads, dev, a, aq)
+    if args.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 2 * x.numel() * 4
+    del c
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(workloads, M, N, K)
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, nvfp4, workloads, dev, a3, aq3):
+    """HBM throughput of the quantizer and the NVFP4 KV-cache round trip."""
+    res = {}
+    # activation quantize of the FFN down-projection input (bf16 [16384, 14336], 470 MB)
+    a4 = workloads.activations(4).to(dev)
+    M4, K4 = a4.shape
+    q4 = (torch.empty(M4, K4 // 2, dtype=torch.uint8, device=dev),
+          torch.empty(M4, K4 // 16, dtype=torch.uint8, device=dev),
+          torch.empty(1, dtype=torch.float32, device=dev))
+    ms = time_calls(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2]), 10, 2)
+    n = a4.numel()
+    res["quantize_ffn_down_act"] = {"shape": [M4, K4], "ms": round(ms, 4),
+                                    "GB/s": round(n * (B_AMAX + B_ENCODE) / (ms * 1e-3) / 1e9, 1),
+                                    "bytes_per_elem": B_AMAX + B_ENCODE}
+    del a4, q4
+    # NVFP4 KV cache: K and V bf16 [24, 65536, 128], quantize + dequantize
+    k, v = workloads.kv_cache()
+    k, v = k.to(dev), v.to(dev)
+    H, T, D = k.shape
+    qk, qv = nvfp4.kv_quantize(k), nvfp4.kv_quantize(v)
+    ok, ov = torch.empty_like(k), torch.empty_like(v)
+
+    def rt():
+        nvfp4.kv_quantize(k, out=qk)
+        nvfp4.kv_quantize(v, out=qv)
+        nvfp4.kv_dequantize(*qk, out=ok)
+        nvfp4.kv_dequantize(*qv, out=ov)
+
+    ms = time_calls(torch, rt, 10, 2)
+    n = 2 * k.numel()
+    res["kv_cache_roundtrip"] = {"shape": [H, T, D], "tensors": 2, "ms": round(ms, 4),
+                                 "GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (ms * 1e-3) / 1e9, 1),
+                                 "bytes": n * (B_AMAX + B_ENCODE + B_DEQUANT)}
+    ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
+    ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
+    res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}
+    res["kv_dequantize"] = {"ms": round(ms_d, 4), "GB/s": round(k.numel() * B_DEQUANT / (ms_d * 1e-3) / 1e9, 1)}
+    res["hbm_peak_GB/s"] = HBM_PEAK_GBS
+    log("secondary", json.dumps(res))
+    return res
+
+
+def cpu_baseline(workloads, M, N, K, rows=1024):
+    """The CPU oracle (test infrastructure) on a bounded sample of the step:
+    quantize `rows` activation rows with the tensor's s_g and compute their
+    reference GEMM rows against all N weight rows (weights quantized once,
+    not timed), as TFLOP/s of the same 2 M N K metric."""
+    import numpy as np
+    import oracle
+
+    a = workloads.bf16_bits(workloads.activations(3))
+    w = workloads.bf16_bits(workloads.weights(3))
+    wc, ws, wg = oracle.quantize(w)
+    t0 = time.perf_counter()
+    g = oracle.global_scale(oracle.amax(a))
+    ac, as_, _ = oracle.quantize(np.ascontiguousarray(a[:rows]), s_g=g)
+    oracle.gemm_ref(ac, as_, g, wc, ws, wg)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "amax of the full A [%d, %d], quantize of its first %d rows, fp64 reference GEMM of those "
+                      "rows against all %d weight rows (K = %d)" % (M, K, rows, N, K)}
+
+
+if __name__ == "__main__":
+    main()

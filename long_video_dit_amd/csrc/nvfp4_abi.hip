@@ -1,0 +1,170 @@
+// C ABI of the NVFP4 library (include/nvfp4.h): argument validation, then
+// kernel launches on the caller's stream.  Nothing here allocates, copies,
+// synchronizes or reads device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/nvfp4.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace nvfp4
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_dtype(int d) { return d == nvfp4::kDtypeF32 || d == nvfp4::kDtypeBf16; }
+
+// rows x k with k % 16 == 0, within the size limit.
+nvfp4_status_t check_matrix(int64_t rows, int64_t k, bool rows_may_be_zero) {
+  if (rows < 0 || (rows == 0 && !rows_may_be_zero) || k <= 0 || k % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (k > kMaxElems || (rows > 0 && rows > kMaxElems / k)) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+nvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (sizes must be positive, k a multiple of 16, within limits)";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer (data 16-byte, scales and s_g 4-byte aligned)";
+    case NVFP4_ERR_DTYPE: return "unknown dtype";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    case NVFP4_ERR_FLAGS: return "unknown flags";
+    default: return "unknown status";
+  }
+}
+
+nvfp4_status_t nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
+                              float* s_g, int flags, void* stream) {
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  nvfp4_status_t st = check_matrix(rows, k, true);
+  if (st != NVFP4_OK) return st;
+  if (!s_g || (rows > 0 && (!x || !codes || !scales))) return NVFP4_ERR_NULL;
+  if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t units = rows * k / 8;
+  if (flags == NVFP4_SCALE_COMPUTE) {
+    st = from_hip(nvfp4::launch_global_scale(x, dtype, units, 1, reinterpret_cast<uint32_t*>(codes), units, s_g, s));
+    if (st != NVFP4_OK) return st;
+  }
+  return from_hip(nvfp4::launch_encode(x, dtype, units, 1, s_g, reinterpret_cast<uint32_t*>(codes), scales, s));
+}
+
+nvfp4_status_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t rows,
+                                int64_t k, void* y, int y_dtype, void* stream) {
+  if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_matrix(rows, k, true);
+  if (st != NVFP4_OK) return st;
+  if (!s_g || (rows > 0 && (!codes || !scales || !y))) return NVFP4_ERR_NULL;
+  if (!aligned(s_g, 4) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_dequant(codes, scales, s_g, rows * k / 16, 1, y, y_dtype, (hipStream_t)stream));
+}
+
+static nvfp4_status_t check_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg,
+                                 const uint8_t* b_codes, const uint8_t* b_scales, const float* b_sg, int64_t M,
+                                 int64_t N, int64_t K, const void* c, int c_dtype) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_DTYPE;
+  if (M <= 0 || N <= 0 || M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
+    return NVFP4_ERR_SHAPE;
+  nvfp4_status_t st = check_matrix(M, K, false);
+  if (st == NVFP4_OK) st = check_matrix(N, K, false);
+  if (st == NVFP4_OK && M > kMaxElems / N) st = NVFP4_ERR_SHAPE;
+  if (st != NVFP4_OK) return st;
+  if (!a_codes || !a_scales || !a_sg || !b_codes || !b_scales || !b_sg || !c) return NVFP4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+      !aligned(a_sg, 4) || !aligned(b_sg, 4) || !aligned(c, 16))
+    return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,
+                          const uint8_t* b_scales, const float* b_sg, int64_t M, int64_t N, int64_t K, void* c,
+                          int c_dtype, void* stream) {
+  nvfp4_status_t st = check_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype);
+  if (st != NVFP4_OK) return st;
+  return from_hip(nvfp4::launch_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype,
+                                     (hipStream_t)stream));
+}
+
+nvfp4_status_t nvfp4_gemm_fused_act(const void* a, int a_dtype, int64_t M, int64_t K, float* a_sg, uint8_t* a_codes,
+                                    uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                                    const float* b_sg, int64_t N, void* c, int c_dtype, void* stream) {
+  if (!valid_dtype(a_dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype);
+  if (st != NVFP4_OK) return st;
+  if (!a) return NVFP4_ERR_NULL;
+  if (!aligned(a, 16)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t units = M * K / 8;
+  st = from_hip(nvfp4::launch_global_scale(a, a_dtype, units, 1, reinterpret_cast<uint32_t*>(a_codes), units, a_sg, s));
+  if (st != NVFP4_OK) return st;
+  st = from_hip(nvfp4::launch_encode(a, a_dtype, units, 1, a_sg, reinterpret_cast<uint32_t*>(a_codes), a_scales, s));
+  if (st != NVFP4_OK) return st;
+  return from_hip(nvfp4::launch_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype, s));
+}
+
+static nvfp4_status_t check_kv(int64_t heads, int64_t tokens, int64_t head_dim) {
+  if (heads <= 0 || heads > 65535 || tokens < 0 || head_dim <= 0 || head_dim % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (head_dim > kMaxElems || tokens > kMaxElems / head_dim || heads > kMaxElems / (tokens * head_dim + 1))
+    return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+nvfp4_status_t kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim, uint8_t* codes,
+                           uint8_t* scales, float* head_scales, void* stream) {
+  nvfp4_status_t st = check_kv(heads, tokens, head_dim);
+  if (st != NVFP4_OK) return st;
+  if (!head_scales || (tokens > 0 && (!kv || !codes || !scales))) return NVFP4_ERR_NULL;
+  if (!aligned(head_scales, 4) || !aligned(kv, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t units = tokens * head_dim / 8;
+  st = from_hip(nvfp4::launch_global_scale(kv, nvfp4::kDtypeBf16, units, (int)heads,
+                                           reinterpret_cast<uint32_t*>(codes), units * heads, head_scales, s));
+  if (st != NVFP4_OK) return st;
+  return from_hip(nvfp4::launch_encode(kv, nvfp4::kDtypeBf16, units, (int)heads, head_scales,
+                                       reinterpret_cast<uint32_t*>(codes), scales, s));
+}
+
+nvfp4_status_t kv_dequantize(const uint8_t* codes, const uint8_t* scales, const float* head_scales, int64_t heads,
+                             int64_t tokens, int64_t head_dim, void* kv_out, void* stream) {
+  nvfp4_status_t st = check_kv(heads, tokens, head_dim);
+  if (st != NVFP4_OK) return st;
+  if (!head_scales || (tokens > 0 && (!codes || !scales || !kv_out))) return NVFP4_ERR_NULL;
+  if (!aligned(head_scales, 4) || !aligned(kv_out, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_dequant(codes, scales, head_scales, tokens * head_dim / 16, (int)heads, kv_out,
+                                        nvfp4::kDtypeBf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host-side internals shared by the launchers and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <tuple>
+#include <utility>
+
+namespace nvfp4 {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+
+// Compute-unit count of the current device (cached per device).
+int device_cu_count();
+
+// Launch a kernel through hipLaunchKernel so that the launch status comes back
+// directly (no sticky error state is read or cleared).  Arguments are
+// converted to the kernel's parameter types before their addresses are taken.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count mismatch");
+  std::tuple<P...> t(std::forward<A>(args)...);
+  return std::apply(
+      [&](auto&... a) {
+        void* ptrs[] = {(void*)&a..., nullptr};
+        return hipLaunchKernel((const void*)kernel, grid, block, ptrs, shmem, stream);
+      },
+      t);
+}
+
+// Quantizer launchers (nvfp4_quant.hip).  A tensor is `groups` runs of
+// units_per_group 8-element units, each run with its own s_g.
+hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group, int groups, uint32_t* partials,
+                               int64_t partial_capacity, float* s_g, hipStream_t stream);
+hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
+                         uint32_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
+                          int groups, void* y, int y_dtype, hipStream_t stream);
+
+// W4A4 GEMM launcher (nvfp4_gemm.hip).
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_sg, int64_t M, int64_t N, int64_t K, void* c,
+                       int c_dtype, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,269 @@
+// NVFP4 quantize / dequantize kernels for gfx950 (MI355X).
+//
+// Layout: a tensor is processed as G equal groups (G = 1 for a plain
+// tensor, G = heads for the KV cache), each group a flat run of elements
+// with its own fp32 scale.  Inside a group the work unit of one lane is 8
+// consecutive elements (16 B of bf16, 32 B of fp32); lanes 2j and 2j+1 own
+// one 16-element block and exchange their partial block maximum with one
+// cross-lane move.  All kernels are HBM-bound grid-stride loops.
+//
+//   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
+//   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
+//   encode_kernel        pass 2: scale byte per 16, 8 codes per lane
+//   dequant_kernel       codes + scales -> bf16 / fp32
+//
+// The amax partials live in the caller's codes buffer (it is at least 4 B
+// per 8 elements), which the encode pass overwrites afterwards; the calls
+// therefore need no workspace and no atomics, and the scale is deterministic.
+#include <hip/hip_runtime.h>
+
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+constexpr int kThreads = 256;
+
+// ---- element loads: 8 consecutive elements as fp32 -----------------------
+
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ x, int64_t unit, float (&f)[8]) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + unit);
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16);
+  f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16);
+  f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void load8(const float* __restrict__ x, int64_t unit, float (&f)[8]) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(x) + 2 * unit;
+  const f32x4 a = __builtin_nontemporal_load(p);
+  const f32x4 b = __builtin_nontemporal_load(p + 1);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// max |x| of 8 elements as non-negative fp32 bits (integer order = float order)
+__device__ __forceinline__ uint32_t amax8_bits(const uint16_t* __restrict__ x, int64_t unit) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + unit);
+  uint32_t m = 0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    m = __builtin_elementwise_max(m, w[i] & 0x7fffu);
+    m = __builtin_elementwise_max(m, (w[i] >> 16) & 0x7fffu);
+  }
+  return m << 16;
+}
+
+__device__ __forceinline__ uint32_t amax8_bits(const float* __restrict__ x, int64_t unit) {
+  float f[8];
+  load8(x, unit, f);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = __builtin_elementwise_max(m, __float_as_uint(f[i]) & 0x7fffffffu);
+  return m;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* smem) {
+  // wavefront reduction, then across the 4 waves of the block
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_elementwise_max(v, (uint32_t)__shfl_xor((int)v, off));
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (lane == 0) smem[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kThreads / 64; i++) v = __builtin_elementwise_max(v, smem[i]);
+  }
+  return v;
+}
+
+// grid: (P, G).  Block b of group g reduces units b*? grid-stride and writes
+// partials[g * P + b].
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const T* __restrict__ x, int64_t units_per_group,
+                                                                uint32_t* __restrict__ partials) {
+  __shared__ uint32_t smem[kThreads / 64];
+  const int g = blockIdx.y;
+  const T* xg = x + (int64_t)g * units_per_group * 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; u + 3 * stride < units_per_group; u += 4 * stride) {
+    const uint32_t a = amax8_bits(xg, u), b = amax8_bits(xg, u + stride);
+    const uint32_t c = amax8_bits(xg, u + 2 * stride), d = amax8_bits(xg, u + 3 * stride);
+    m = __builtin_elementwise_max(m, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                                               __builtin_elementwise_max(c, d)));
+  }
+  for (; u < units_per_group; u += stride) m = __builtin_elementwise_max(m, amax8_bits(xg, u));
+  m = block_max_u32(m, smem);
+  if (threadIdx.x == 0) partials[(int64_t)g * gridDim.x + blockIdx.x] = m;
+}
+
+// grid: G blocks.  s_g[g] = RN_f32(max(partials of g) / 2688).
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t* __restrict__ partials, int P,
+                                                            float* __restrict__ s_g) {
+  __shared__ uint32_t smem[kThreads / 64];
+  const int g = blockIdx.x;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < P; i += kThreads) m = __builtin_elementwise_max(m, partials[(int64_t)g * P + i]);
+  m = block_max_u32(m, smem);
+  if (threadIdx.x == 0) {
+    // IEEE division is correctly rounded: one RNE of amax / 2688.
+    s_g[g] = __fdiv_rn(__uint_as_float(m), 2688.0f);
+  }
+}
+
+// grid: (X, G).  Each lane encodes 8-element units; the partner lane (lane ^ 1)
+// holds the other half of the 16-element block.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, int64_t units_per_group,
+                                                          const float* __restrict__ s_g,
+                                                          uint32_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int g = blockIdx.y;
+  const EncodeConsts c = make_encode_consts(s_g[g]);
+  const int64_t base = (int64_t)g * units_per_group;
+  const T* xg = x + base * 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int U = 2;
+  for (int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; u0 < units_per_group; u0 += U * stride) {
+    float f[U][8];
+    bool ok[U];
+#pragma unroll
+    for (int j = 0; j < U; j++) {
+      const int64_t u = u0 + j * stride;
+      ok[j] = u < units_per_group;  // uniform across the lane pair (units_per_group is even)
+      if (ok[j]) load8(xg, u, f[j]);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) f[j][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; j++) {
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 1));
+      const uint32_t sb = encode_scale(am, c);
+      const uint32_t w = encode8(f[j], sb, c);
+      if (ok[j]) {
+        const int64_t u = u0 + j * stride;
+        codes[base + u] = w;
+        if ((threadIdx.x & 1) == 0) scales[(base + u) >> 1] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// grid: (X, G).  One lane per 16-element block: 8 code bytes + 1 scale byte
+// -> 16 outputs.
+// val(code) of the two nibbles of byte S of w, times the block scale (exact).
+template <int S>
+__device__ __forceinline__ void decode_pair(uint32_t w, float sv, float* p) {
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, S);
+  p[0] = d.x * sv;
+  p[1] = d.y * sv;
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const u32x2* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           int64_t blocks_per_group, const float* __restrict__ s_g,
+                                                           void* __restrict__ y) {
+  const int g = blockIdx.y;
+  const float sg = s_g[g];
+  const int64_t base = (int64_t)g * blocks_per_group;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < blocks_per_group; b += stride) {
+    const u32x2 w = __builtin_nontemporal_load(codes + base + b);
+    const float sv = e4m3_value(scales[base + b]);
+    float p[16];  // val(code) * val(scale), exact: <= 6 significant bits
+    decode_pair<0>(w.x, sv, p + 0);
+    decode_pair<1>(w.x, sv, p + 2);
+    decode_pair<2>(w.x, sv, p + 4);
+    decode_pair<3>(w.x, sv, p + 6);
+    decode_pair<0>(w.y, sv, p + 8);
+    decode_pair<1>(w.y, sv, p + 10);
+    decode_pair<2>(w.y, sv, p + 12);
+    decode_pair<3>(w.y, sv, p + 14);
+    if constexpr (kBf16Out) {
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) o[i] = bf16_of_product(p[2 * i], sg) | (bf16_of_product(p[2 * i + 1], sg) << 16);
+      u32x4* dst = reinterpret_cast<u32x4*>(y) + 2 * (base + b);
+      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst);
+      __builtin_nontemporal_store(u32x4{o[4], o[5], o[6], o[7]}, dst + 1);
+    } else {
+      f32x4* dst = reinterpret_cast<f32x4*>(y) + 4 * (base + b);
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        __builtin_nontemporal_store(f32x4{p[4 * q] * sg, p[4 * q + 1] * sg, p[4 * q + 2] * sg, p[4 * q + 3] * sg},
+                                    dst + q);
+    }
+  }
+}
+
+// ---- launchers ----------------------------------------------------------
+
+static int grid_blocks(int64_t work_items, int per_thread, int max_blocks) {
+  int64_t b = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  if (b < 1) b = 1;
+  if (b > max_blocks) b = max_blocks;
+  return (int)b;
+}
+
+hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group, int groups, uint32_t* partials,
+                               int64_t partial_capacity, float* s_g, hipStream_t stream) {
+  const int cus = device_cu_count();
+  // Partials per group: enough blocks to saturate HBM, bounded by the scratch.
+  int64_t P = grid_blocks(units_per_group, 8, (int)std::max<int64_t>(1, (int64_t)cus * 8 / groups));
+  if (P * groups > partial_capacity) P = std::max<int64_t>(1, partial_capacity / groups);
+  if (units_per_group == 0) {
+    P = 0;
+  } else {
+    const dim3 grid((unsigned)P, (unsigned)groups);
+    hipError_t e;
+    if (dtype == kDtypeF32)
+      e = launch_kernel(amax_partial_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group,
+                        partials);
+    else
+      e = launch_kernel(amax_partial_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x,
+                        units_per_group, partials);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel(finalize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, (const uint32_t*)partials,
+                       (int)P, s_g);
+}
+
+hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
+                         uint32_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (units_per_group == 0) return hipSuccess;
+  const int cus = device_cu_count();
+  const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 16 / groups));
+  const dim3 grid((unsigned)bx, (unsigned)groups);
+  if (dtype == kDtypeF32)
+    return launch_kernel(encode_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group, s_g,
+                         codes, scales);
+  return launch_kernel(encode_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, units_per_group,
+                       s_g, codes, scales);
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
+                          int groups, void* y, int y_dtype, hipStream_t stream) {
+  if (blocks_per_group == 0) return hipSuccess;
+  const int cus = device_cu_count();
+  const int bx = grid_blocks(blocks_per_group, 1, std::max(1, cus * 16 / groups));
+  const dim3 grid((unsigned)bx, (unsigned)groups);
+  if (y_dtype == kDtypeF32)
+    return launch_kernel(dequant_kernel<false>, grid, dim3(kThreads), 0, stream, (const u32x2*)codes, scales,
+                         blocks_per_group, s_g, y);
+  return launch_kernel(dequant_kernel<true>, grid, dim3(kThreads), 0, stream, (const u32x2*)codes, scales,
+                       blocks_per_group, s_g, y);
+}
+
+}  // namespace nvfp4
