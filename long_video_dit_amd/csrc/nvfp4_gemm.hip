@@ -27,25 +27,52 @@
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
+#ifndef NVFP4_GEMM_WM
+#define NVFP4_GEMM_WM 2
+#define NVFP4_GEMM_WN 2
+#endif
+#ifndef NVFP4_GEMM_FAST_WM
+#define NVFP4_GEMM_FAST_WM 2
+#define NVFP4_GEMM_FAST_WN 2
+#endif
+
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kKC = 128;
-constexpr int kGemmThreads = 256;
+constexpr int kTile = 256;  // rows of A and of B per workgroup tile
+constexpr int kKC = 128;    // K per LDS stage
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
+// LDS planes are padded by 64 B so that the 16-byte stores of 4 threads
+// sharing a row (one per plane) and the 16-byte operand reads of 16
+// consecutive rows both spread over all 64 banks.
+constexpr int kPlaneStride = kTile + 4;  // uint4 units
+
 struct GemmSmem {
-  uint4 a_codes[2][4 * 256];  // [stage][plane q = 2 s + h][row] 16 B
-  uint4 b_codes[2][4 * 256];
-  uint2 a_scales[2][256];     // [stage][row] the chunk's 8 scale bytes
-  uint2 b_scales[2][256];
+  uint4 a_codes[2][4 * kPlaneStride];  // [stage][plane q = 2 s + h][row] 16 B
+  uint4 b_codes[2][4 * kPlaneStride];
+  uint32_t a_scales[2][4][kTile];      // [stage][q][row] fp16 scales of blocks 2q, 2q+1
+  uint32_t b_scales[2][4][kTile];
 };
 
+// Wave layout: WM x WN waves, each FM x FN MFMA tiles of 32 x 32, covering
+// the 256 x 256 workgroup tile.
+template <int WM, int WN>
+struct GemmCfg {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int FM = kTile / (32 * WM);
+  static constexpr int FN = kTile / (32 * WN);
+  static constexpr int kPieces = 4 * kTile / kThreads;  // 16-byte code pieces per thread per operand
+  static constexpr int kScaleRows = 2 * kTile / kThreads;  // scale rows (A then B) per thread
+};
+
+template <typename C>
 struct Staged {
-  uint4 a[4], b[4];
-  uint2 sa, sb;
+  uint4 a[C::kPieces], b[C::kPieces];
+  uint2 s[C::kScaleRows];
 };
 
 // 16 bytes of codes of row `row` at byte offset `off` in the row; zero past K.
@@ -72,6 +99,7 @@ __device__ __forceinline__ uint4 load_codes(const uint8_t* __restrict__ p, int64
   }
 }
 
+// The 8 scale bytes of chunk kc of row `row`; zero past K.
 template <bool kFast>
 __device__ __forceinline__ uint2 load_scales(const uint8_t* __restrict__ p, int64_t row, int64_t rows, int K,
                                              int kc) {
@@ -88,8 +116,11 @@ __device__ __forceinline__ uint2 load_scales(const uint8_t* __restrict__ p, int6
   }
 }
 
-template <bool kFast>
-__device__ __forceinline__ void load_chunk(Staged& st, const uint8_t* __restrict__ a_codes,
+// Global -> registers for chunk kc: thread t loads 16-byte pieces
+// (row = p / 4, plane q = p % 4) for p = t + kThreads * i, which gives four
+// consecutive threads 64 contiguous bytes of a row.
+template <typename C, bool kFast>
+__device__ __forceinline__ void load_chunk(Staged<C>& st, const uint8_t* __restrict__ a_codes,
                                            const uint8_t* __restrict__ a_scales, const uint8_t* __restrict__ b_codes,
                                            const uint8_t* __restrict__ b_scales, int64_t m0, int64_t n0, int M, int N,
                                            int K, int kc) {
@@ -97,26 +128,50 @@ __device__ __forceinline__ void load_chunk(Staged& st, const uint8_t* __restrict
   const int q = t & 3;
   const int off = kc * (kKC / 2) + 16 * q;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int row = (t >> 2) + 64 * i;
+  for (int i = 0; i < C::kPieces; i++) {
+    const int row = (t >> 2) + (C::kThreads / 4) * i;
     st.a[i] = load_codes<kFast>(a_codes, m0 + row, M, K, off);
     st.b[i] = load_codes<kFast>(b_codes, n0 + row, N, K, off);
   }
-  st.sa = load_scales<kFast>(a_scales, m0 + t, M, K, kc);
-  st.sb = load_scales<kFast>(b_scales, n0 + t, N, K, kc);
+#pragma unroll
+  for (int i = 0; i < C::kScaleRows; i++) {
+    const int row = t + C::kThreads * i;  // 0..255: A rows, 256..511: B rows
+    st.s[i] = row < kTile ? load_scales<kFast>(a_scales, m0 + row, M, K, kc)
+                          : load_scales<kFast>(b_scales, n0 + row - kTile, N, K, kc);
+  }
 }
 
-__device__ __forceinline__ void store_chunk(const Staged& st, GemmSmem& sm, int stage) {
+// Two E4M3 scale bytes -> two exact fp16 values: the byte shifted into an
+// fp16 bit pattern (exponent bits 6:3 -> 14:10, mantissa -> 9:7) reads as
+// 2^-8 times the E4M3 value, subnormals included; one packed multiply by 256
+// restores it.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t b0, uint32_t b1) {
+  const f16x2 v = __builtin_bit_cast(f16x2, (b0 << 7) | (b1 << 23)) * f16x2{(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename C>
+__device__ __forceinline__ void store_chunk(const Staged<C>& st, GemmSmem& sm, int stage) {
   const int t = threadIdx.x;
   const int q = t & 3;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int row = (t >> 2) + 64 * i;
-    sm.a_codes[stage][q * 256 + row] = st.a[i];
-    sm.b_codes[stage][q * 256 + row] = st.b[i];
+  for (int i = 0; i < C::kPieces; i++) {
+    const int row = (t >> 2) + (C::kThreads / 4) * i;
+    sm.a_codes[stage][q * kPlaneStride + row] = st.a[i];
+    sm.b_codes[stage][q * kPlaneStride + row] = st.b[i];
   }
-  sm.a_scales[stage][t] = st.sa;
-  sm.b_scales[stage][t] = st.sb;
+#pragma unroll
+  for (int i = 0; i < C::kScaleRows; i++) {
+    const int row = t + C::kThreads * i;
+    uint32_t(*dst)[kTile] = row < kTile ? sm.a_scales[stage] : sm.b_scales[stage];
+    const int rr = row & (kTile - 1);
+    const uint32_t w[2] = {st.s[i].x, st.s[i].y};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t b = w[j / 2] >> (16 * (j & 1));
+      dst[j][rr] = e4m3x2_to_f16x2(b & 0xffu, (b >> 8) & 0xffu);
+    }
+  }
 }
 
 // 8 E2M1 codes (one 32-bit word, element e in bits 4e+3..4e) times an fp16
@@ -127,11 +182,6 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 sc) {
   const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
   const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
   return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-__device__ __forceinline__ f16x2 scale_f16x2(uint32_t byte) {
-  const _Float16 v = (_Float16)e4m3_value(byte);  // exact: E4M3 values fit fp16
-  return f16x2{v, v};
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int t) {
@@ -154,71 +204,73 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
   tn = in_group / gm;
 }
 
-template <bool kFast, bool kBf16Out>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_w4a4_kernel(
+template <int WM, int WN, bool kFast, bool kBf16Out>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const float* __restrict__ b_sg, int M,
     int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
+  using C = GemmCfg<WM, WN>;
+  constexpr int FM = C::FM, FN = C::FN;
   __shared__ GemmSmem sm;
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   const int nk = (K + kKC - 1) / kKC;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int r = lane & 31, h = lane >> 5;
 
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < FM; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; j++) acc[i][j] = f32x16{};
 
-  Staged st;
-  load_chunk<kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, 0);
-  store_chunk(st, sm, 0);
-  if (nk > 1) load_chunk<kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, 1);
+  Staged<C> st;
+  load_chunk<C, kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, 0);
+  store_chunk<C>(st, sm, 0);
+  if (nk > 1) load_chunk<C, kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, 1);
   __syncthreads();
 
   for (int kc = 0; kc < nk; kc++) {
     const int cur = kc & 1;
-    if (kc + 1 < nk) store_chunk(st, sm, cur ^ 1);
-    if (kc + 2 < nk) load_chunk<kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+    if (kc + 1 < nk) store_chunk<C>(st, sm, cur ^ 1);
+    if (kc + 2 < nk) load_chunk<C, kFast>(st, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
 #pragma unroll
     for (int s = 0; s < 2; s++) {
       const int q = 2 * s + h;
-      uint4 ca[4], cb[4];
-      f16x2 sa_lo[4], sa_hi[4], sb_lo[4], sb_hi[4];
+      uint4 ca[FM], cb[FN];
+      f16x2 sa[FM], sb[FN];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int row = wm * 128 + 32 * i + r;
-        ca[i] = sm.a_codes[cur][q * 256 + row];
-        const uint2 s8 = sm.a_scales[cur][row];
-        const uint32_t pair = ((q < 2 ? s8.x : s8.y) >> (16 * (q & 1))) & 0xffffu;
-        sa_lo[i] = scale_f16x2(pair & 0xffu);
-        sa_hi[i] = scale_f16x2(pair >> 8);
+      for (int i = 0; i < FM; i++) {
+        const int row = wm * (32 * FM) + 32 * i + r;
+        ca[i] = sm.a_codes[cur][q * kPlaneStride + row];
+        sa[i] = __builtin_bit_cast(f16x2, sm.a_scales[cur][q][row]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int row = wn * 128 + 32 * j + r;
-        cb[j] = sm.b_codes[cur][q * 256 + row];
-        const uint2 s8 = sm.b_scales[cur][row];
-        const uint32_t pair = ((q < 2 ? s8.x : s8.y) >> (16 * (q & 1))) & 0xffffu;
-        sb_lo[j] = scale_f16x2(pair & 0xffu);
-        sb_hi[j] = scale_f16x2(pair >> 8);
+      for (int j = 0; j < FN; j++) {
+        const int row = wn * (32 * FN) + 32 * j + r;
+        cb[j] = sm.b_codes[cur][q * kPlaneStride + row];
+        sb[j] = __builtin_bit_cast(f16x2, sm.b_scales[cur][q][row]);
       }
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        f16x8 av[4], bv[4];
+        f16x8 av[FM], bv[FN];
 #pragma unroll
-        for (int i = 0; i < 4; i++) av[i] = decode8(word_of(ca[i], t), t < 2 ? sa_lo[i] : sa_hi[i]);
+        for (int i = 0; i < FM; i++) {
+          const _Float16 sc = t < 2 ? sa[i].x : sa[i].y;
+          av[i] = decode8(word_of(ca[i], t), f16x2{sc, sc});
+        }
 #pragma unroll
-        for (int j = 0; j < 4; j++) bv[j] = decode8(word_of(cb[j], t), t < 2 ? sb_lo[j] : sb_hi[j]);
+        for (int j = 0; j < FN; j++) {
+          const _Float16 sc = t < 2 ? sb[j].x : sb[j].y;
+          bv[j] = decode8(word_of(cb[j], t), f16x2{sc, sc});
+        }
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < FM; i++)
 #pragma unroll
-          for (int j = 0; j < 4; j++)
+          for (int j = 0; j < FN; j++)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
     }
@@ -229,13 +281,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_w4a4_kernel(
   // column r of the 32 x 32 tile.
   const float g = a_sg[0] * b_sg[0];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < FM; i++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t col = n0 + wn * 128 + 32 * j + r;
+    for (int j = 0; j < FN; j++) {
+      const int64_t col = n0 + wn * (32 * FN) + 32 * j + r;
 #pragma unroll
       for (int e = 0; e < 16; e++) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
+        const int64_t row = m0 + wm * (32 * FM) + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
         if (row < M && col < N) {
           const float v = acc[i][j][e] * g;
           if constexpr (kBf16Out)
@@ -248,19 +300,253 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_w4a4_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (K % 512 == 0, N % 4 == 0, aligned operands): the packed operands
+// go global -> LDS with global_load_lds_dwordx4 (no register staging, no LDS
+// stores), two LDS stages of K = 256 held in two distinct LDS objects so the
+// compiler can tell the prefetch of one stage from the reads of the other.
+// Per stage and operand: codes [256 rows][8 slots of 16 B] (256 codes per
+// row) with slot = plane q ^ ((row / 2) % 8), which makes both the 128 B
+// per-row coalesced fills and the 16-row operand reads bank-conflict free;
+// raw scale bytes [256 rows][4 dwords] (dword swizzled by row / 16), turned
+// into fp16 pairs when read.  The MFMA takes B as its
+// first operand, so every lane ends with 4 consecutive output columns of one
+// row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per instruction.
+// Rows past M or N are clamped to the last row: they only feed outputs that
+// are never stored.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// global -> LDS copy of 16 (or 4) bytes per lane: lane i reads base +
+// voff[i] and writes LDS address lds_base + 16 i (or 4 i); lds_base and base
+// are wave-uniform (M0 and an SGPR pair).  Issued as asm statements without
+// outputs so that the compiler does not track these LDS writes (its tracking
+// falls back to waiting for every outstanding copy before any LDS read, which
+// would serialize the prefetch); completion is enforced explicitly with
+// s_waitcnt vmcnt(0) + s_barrier before a stage is read.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
+}
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
+}
+
+constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code bytes per row
+
+struct __attribute__((aligned(16))) FastStage {
+  uint8_t a_codes[kTile * 128];  // [row][8 slots of 16 B], slot = plane q ^ ((row / 2) % 8)
+  uint8_t b_codes[kTile * 128];
+  uint8_t a_scales[kTile * 16];  // [row][4 dwords], dword = d ^ ((row / 16) % 4)
+  uint8_t b_scales[kTile * 16];
+};
+
+// Per-lane byte offsets (row clamped to the last valid row, plane slot
+// swizzle applied) of the copies one thread issues per stage; computed once
+// per tile.  Offsets are 32-bit: the fast path requires operands < 4 GiB.
+template <int W>
+struct FastOffsets {
+  static constexpr int kCodeInsts = 32 / W;  // 2048 pieces of 16 B per operand, 64 per instruction
+  static constexpr int kScaleInsts = 16 / W;  // 1024 dwords of scales per operand
+  uint32_t a[kCodeInsts], b[kCodeInsts], sa[kScaleInsts], sb[kScaleInsts];
+};
+
+template <int W>
+__device__ __forceinline__ void fast_offsets(FastOffsets<W>& o, int64_t m0, int64_t n0, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
+#pragma unroll
+  for (int i = 0; i < FastOffsets<W>::kCodeInsts; i++) {
+    const int slot = (w * FastOffsets<W>::kCodeInsts + i) * 64 + lane;
+    const int row = slot >> 3;
+    const uint32_t q = (slot & 7) ^ ((row >> 1) & 7);
+    const uint32_t ra = (uint32_t)(m0 + row < M ? m0 + row : M - 1);
+    const uint32_t rb = (uint32_t)(n0 + row < N ? n0 + row : N - 1);
+    o.a[i] = ra * row_bytes + 16 * q;
+    o.b[i] = rb * row_bytes + 16 * q;
+  }
+#pragma unroll
+  for (int i = 0; i < FastOffsets<W>::kScaleInsts; i++) {
+    const int d = (w * FastOffsets<W>::kScaleInsts + i) * 64 + lane;
+    const int row = d >> 2;
+    const uint32_t dw = (d & 3) ^ ((row >> 4) & 3);
+    const uint32_t ra = (uint32_t)(m0 + row < M ? m0 + row : M - 1);
+    const uint32_t rb = (uint32_t)(n0 + row < N ? n0 + row : N - 1);
+    o.sa[i] = ra * srow_bytes + 4 * dw;
+    o.sb[i] = rb * srow_bytes + 4 * dw;
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void fast_load_stage(FastStage& S, const FastOffsets<W>& o,
+                                                const uint8_t* __restrict__ a_codes,
+                                                const uint8_t* __restrict__ a_scales,
+                                                const uint8_t* __restrict__ b_codes,
+                                                const uint8_t* __restrict__ b_scales, int kc) {
+  const int w = threadIdx.x >> 6;
+  const uint8_t* ac = a_codes + (size_t)kc * 128;
+  const uint8_t* bc = b_codes + (size_t)kc * 128;
+  const uint8_t* as = a_scales + (size_t)kc * 16;
+  const uint8_t* bs = b_scales + (size_t)kc * 16;
+#pragma unroll
+  for (int i = 0; i < FastOffsets<W>::kCodeInsts; i++) {
+    const int slot0 = (w * FastOffsets<W>::kCodeInsts + i) * 64;
+    lds_dma16(ac, o.a[i], S.a_codes + slot0 * 16);
+    lds_dma16(bc, o.b[i], S.b_codes + slot0 * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < FastOffsets<W>::kScaleInsts; i++) {
+    const int d0 = (w * FastOffsets<W>::kScaleInsts + i) * 64;
+    lds_dma4(as, o.sa[i], S.a_scales + d0 * 4);
+    lds_dma4(bs, o.sb[i], S.b_scales + d0 * 4);
+  }
+}
+
+// Scale bytes of plane q (blocks 2q, 2q+1) of a row, as two fp16 values.
+__device__ __forceinline__ uint32_t fast_scale_pair(const uint8_t* scales, int row, int q) {
+  const int dw = (q >> 1) ^ ((row >> 4) & 3);
+  const uint32_t b2 = *reinterpret_cast<const uint16_t*>(scales + row * 16 + 4 * dw + 2 * (q & 1));
+  return e4m3x2_to_f16x2(b2 & 0xffu, b2 >> 8);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&acc)[FN][FM], int wm, int wn, int r,
+                                                   int h) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const int q = 2 * s + h;
+    uint4 ca[FM], cb[FN];
+    uint32_t sa[FM], sb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+      const int row = wm * (32 * FM) + 32 * i + r;
+      ca[i] = *reinterpret_cast<const uint4*>(S.a_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
+      sa[i] = fast_scale_pair(S.a_scales, row, q);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+      const int row = wn * (32 * FN) + 32 * j + r;
+      cb[j] = *reinterpret_cast<const uint4*>(S.b_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
+      sb[j] = fast_scale_pair(S.b_scales, row, q);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      f16x8 av[FM], bv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; i++) {
+        const f16x2 s2 = __builtin_bit_cast(f16x2, sa[i]);
+        const _Float16 sc = t < 2 ? s2.x : s2.y;
+        av[i] = decode8(word_of(ca[i], t), f16x2{sc, sc});
+      }
+#pragma unroll
+      for (int j = 0; j < FN; j++) {
+        const f16x2 s2 = __builtin_bit_cast(f16x2, sb[j]);
+        const _Float16 sc = t < 2 ? s2.x : s2.y;
+        bv[j] = decode8(word_of(cb[j], t), f16x2{sc, sc});
+      }
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
+    }
+  }
+}
+
+template <int WM, int WN, bool kBf16Out>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_fast_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const float* __restrict__ b_sg, int M,
+    int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
+  constexpr int W = WM * WN;
+  constexpr int FM = kTile / (32 * WM), FN = kTile / (32 * WN);
+  __shared__ FastStage st0;
+  __shared__ FastStage st1;
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  const int nk = K / kFastKC;  // even
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, h = lane >> 5;
+
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int j = 0; j < FN; j++)
+#pragma unroll
+    for (int i = 0; i < FM; i++) acc[j][i] = f32x16{};
+
+  FastOffsets<W> off;
+  fast_offsets<W>(off, m0, n0, M, N, K);
+  fast_load_stage<W>(st0, off, a_codes, a_scales, b_codes, b_scales, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; kc += 2) {
+    fast_load_stage<W>(st1, off, a_codes, a_scales, b_codes, b_scales, kc + 1);
+    fast_compute_stage<FM, FN>(st0, acc, wm, wn, r, h);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kc + 2 < nk) fast_load_stage<W>(st0, off, a_codes, a_scales, b_codes, b_scales, kc + 2);
+    fast_compute_stage<FM, FN>(st1, acc, wm, wn, r, h);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Epilogue: lane (r, h), accumulator element e of tile (j, i) is output row
+  // m = 32 i + r and column n = 32 j + 8 (e / 4) + 4 h + e % 4.
+  const float g = a_sg[0] * b_sg[0];
+#pragma unroll
+  for (int i = 0; i < FM; i++) {
+    const int64_t m = m0 + wm * (32 * FM) + 32 * i + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int64_t n = n0 + wn * (32 * FN) + 32 * j + 8 * gq + 4 * h;
+        if (n >= N) continue;  // N % 4 == 0: the 4 columns are all in or all out
+        const float v0 = acc[j][i][4 * gq] * g, v1 = acc[j][i][4 * gq + 1] * g;
+        const float v2 = acc[j][i][4 * gq + 2] * g, v3 = acc[j][i][4 * gq + 3] * g;
+        if constexpr (kBf16Out) {
+          const bf16x2 p0 = {(__bf16)v0, (__bf16)v1}, p1 = {(__bf16)v2, (__bf16)v3};
+          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + m * N + n) =
+              u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(c) + m * N + n) = f32x4{v0, v1, v2, v3};
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_sg, int64_t M, int64_t N, int64_t K, void* c,
                        int c_dtype, hipStream_t stream) {
-  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
+  constexpr int WM = NVFP4_GEMM_WM, WN = NVFP4_GEMM_WN;
+  const int tiles_m = (int)((M + kTile - 1) / kTile), tiles_n = (int)((N + kTile - 1) / kTile);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
   const bool fast = (K % kKC == 0) && ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)b_codes % 16 == 0) &&
                     ((uintptr_t)a_scales % 8 == 0) && ((uintptr_t)b_scales % 8 == 0);
   const bool bf = c_dtype == kDtypeBf16;
-#define NVFP4_GEMM_LAUNCH(F, B)                                                                                    \
-  launch_kernel(gemm_w4a4_kernel<F, B>, grid, block, 0, stream, a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, \
-                (int)M, (int)N, (int)K, c, tiles_m, tiles_n)
+  const bool dma = (K % (2 * kFastKC) == 0) && (N % 4 == 0) && (M * (K / 2) < (int64_t(1) << 32)) &&
+                   (N * (K / 2) < (int64_t(1) << 32)) && ((uintptr_t)a_codes % 16 == 0) &&
+                   ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 4 == 0) &&
+                   ((uintptr_t)b_scales % 4 == 0) && ((uintptr_t)c % 16 == 0);
+  if (dma) {
+    constexpr int FWM = NVFP4_GEMM_FAST_WM, FWN = NVFP4_GEMM_FAST_WN;
+    const dim3 fblock(64 * FWM * FWN);
+    if (bf)
+      return launch_kernel(gemm_w4a4_fast_kernel<FWM, FWN, true>, grid, fblock, 0, stream, a_codes, a_scales, a_sg,
+                           b_codes, b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
+    return launch_kernel(gemm_w4a4_fast_kernel<FWM, FWN, false>, grid, fblock, 0, stream, a_codes, a_scales, a_sg,
+                         b_codes, b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
+  }
+#define NVFP4_GEMM_LAUNCH(F, B)                                                                      \
+  launch_kernel(gemm_w4a4_kernel<WM, WN, F, B>, grid, block, 0, stream, a_codes, a_scales, a_sg, b_codes, \
+                b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n)
   if (fast) return bf ? NVFP4_GEMM_LAUNCH(true, true) : NVFP4_GEMM_LAUNCH(true, false);
   return bf ? NVFP4_GEMM_LAUNCH(false, true) : NVFP4_GEMM_LAUNCH(false, false);
 #undef NVFP4_GEMM_LAUNCH

@@ -25,7 +25,8 @@ def _rand(shape, seed, dtype=torch.bfloat16):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (5, 7, 48), (256, 256, 256), (300, 200, 128), (257, 513, 80),
-                                   (130, 70, 3072), (512, 768, 640)])
+                                   (130, 70, 3072), (512, 768, 640), (300, 200, 512), (1000, 1004, 768),
+                                   (17, 516, 1024), (513, 4, 256)])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_gemm_small_ragged(M, N, K, out):
     log("gemm", M, N, K, out)
