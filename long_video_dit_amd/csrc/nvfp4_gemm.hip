@@ -308,8 +308,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_kernel(
 // Per stage and operand: codes [256 rows][8 slots of 16 B] (256 codes per
 // row) with slot = plane q ^ ((row / 2) % 8), which makes both the 128 B
 // per-row coalesced fills and the 16-row operand reads bank-conflict free;
-// raw scale bytes [256 rows][4 dwords] (dword swizzled by row / 16), turned
-// into fp16 pairs when read.  The MFMA takes B as its
+// raw scale bytes [256 rows][16 B], read as one 16-byte vector per row and
+// stage and turned into fp16 pairs.  The MFMA takes B as its
 // first operand, so every lane ends with 4 consecutive output columns of one
 // row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per instruction.
 // Rows past M or N are clamped to the last row: they only feed outputs that
@@ -337,7 +337,7 @@ constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code byte
 struct __attribute__((aligned(16))) FastStage {
   uint8_t a_codes[kTile * 128];  // [row][8 slots of 16 B], slot = plane q ^ ((row / 2) % 8)
   uint8_t b_codes[kTile * 128];
-  uint8_t a_scales[kTile * 16];  // [row][4 dwords], dword = d ^ ((row / 16) % 4)
+  uint8_t a_scales[kTile * 16];  // [row][16 scale bytes]
   uint8_t b_scales[kTile * 16];
 };
 
@@ -369,7 +369,7 @@ __device__ __forceinline__ void fast_offsets(FastOffsets<W>& o, int64_t m0, int6
   for (int i = 0; i < FastOffsets<W>::kScaleInsts; i++) {
     const int d = (w * FastOffsets<W>::kScaleInsts + i) * 64 + lane;
     const int row = d >> 2;
-    const uint32_t dw = (d & 3) ^ ((row >> 4) & 3);
+    const uint32_t dw = d & 3;
     const uint32_t ra = (uint32_t)(m0 + row < M ? m0 + row : M - 1);
     const uint32_t rb = (uint32_t)(n0 + row < N ? n0 + row : N - 1);
     o.sa[i] = ra * srow_bytes + 4 * dw;
@@ -402,54 +402,80 @@ __device__ __forceinline__ void fast_load_stage(FastStage& S, const FastOffsets<
   }
 }
 
-// Scale bytes of plane q (blocks 2q, 2q+1) of a row, as two fp16 values.
-__device__ __forceinline__ uint32_t fast_scale_pair(const uint8_t* scales, int row, int q) {
-  const int dw = (q >> 1) ^ ((row >> 4) & 3);
-  const uint32_t b2 = *reinterpret_cast<const uint16_t*>(scales + row * 16 + 4 * dw + 2 * (q & 1));
-  return e4m3x2_to_f16x2(b2 & 0xffu, b2 >> 8);
+// The 16 scale bytes of a row (one stage) -> the fp16 scale pairs of the 4
+// planes q = 2 s + h this lane uses (blocks 2q, 2q+1 in dword s, half h).
+__device__ __forceinline__ void fast_scale_pairs(const uint8_t* scales, int row, int h, uint32_t (&p)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(scales + row * 16);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const uint32_t b2 = d[s] >> (16 * h);
+    p[s] = e4m3x2_to_f16x2(b2 & 0xffu, (b2 >> 8) & 0xffu);
+  }
 }
 
 template <int FM, int FN>
+__device__ __forceinline__ void fast_read_codes(const FastStage& S, uint4 (&ca)[FM], uint4 (&cb)[FN], int wm, int wn,
+                                                int r, int q) {
+#pragma unroll
+  for (int i = 0; i < FM; i++) {
+    const int row = wm * (32 * FM) + 32 * i + r;
+    ca[i] = *reinterpret_cast<const uint4*>(S.a_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; j++) {
+    const int row = wn * (32 * FN) + 32 * j + r;
+    cb[j] = *reinterpret_cast<const uint4*>(S.b_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
+  }
+}
+
+// Decode k16-step t of the sub-chunk held in (ca, cb) with its scale pairs.
+template <int FM, int FN>
+__device__ __forceinline__ void fast_decode_step(const uint4 (&ca)[FM], const uint4 (&cb)[FN],
+                                                 const uint32_t (&sa)[FM][4], const uint32_t (&sb)[FN][4], int s,
+                                                 int t, f16x8 (&av)[FM], f16x8 (&bv)[FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; i++) {
+    const f16x2 s2 = __builtin_bit_cast(f16x2, sa[i][s]);
+    const _Float16 sc = t < 2 ? s2.x : s2.y;
+    av[i] = decode8(word_of(ca[i], t), f16x2{sc, sc});
+  }
+#pragma unroll
+  for (int j = 0; j < FN; j++) {
+    const f16x2 s2 = __builtin_bit_cast(f16x2, sb[j][s]);
+    const _Float16 sc = t < 2 ? s2.x : s2.y;
+    bv[j] = decode8(word_of(cb[j], t), f16x2{sc, sc});
+  }
+}
+
+// One stage (K = 256 = 4 sub-chunks x 4 k16-steps), software-pipelined: the
+// codes of sub-chunk s + 1 are read while sub-chunk s is multiplied, and
+// k16-step n + 1 is decoded while the MFMAs of step n run.
+template <int FM, int FN>
 __device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&acc)[FN][FM], int wm, int wn, int r,
                                                    int h) {
+  uint32_t sa[FM][4], sb[FN][4];
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const int q = 2 * s + h;
-    uint4 ca[FM], cb[FN];
-    uint32_t sa[FM], sb[FN];
+  for (int i = 0; i < FM; i++) fast_scale_pairs(S.a_scales, wm * (32 * FM) + 32 * i + r, h, sa[i]);
 #pragma unroll
-    for (int i = 0; i < FM; i++) {
-      const int row = wm * (32 * FM) + 32 * i + r;
-      ca[i] = *reinterpret_cast<const uint4*>(S.a_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
-      sa[i] = fast_scale_pair(S.a_scales, row, q);
+  for (int j = 0; j < FN; j++) fast_scale_pairs(S.b_scales, wn * (32 * FN) + 32 * j + r, h, sb[j]);
+  uint4 ca[2][FM], cb[2][FN];
+  f16x8 av[2][FM], bv[2][FN];
+  fast_read_codes<FM, FN>(S, ca[0], cb[0], wm, wn, r, h);
+  fast_decode_step<FM, FN>(ca[0], cb[0], sa, sb, 0, 0, av[0], bv[0]);
+#pragma unroll
+  for (int n = 0; n < 16; n++) {
+    const int s = n >> 2, t = n & 3;
+    if (t == 0 && s < 3) fast_read_codes<FM, FN>(S, ca[(s + 1) & 1], cb[(s + 1) & 1], wm, wn, r, 2 * (s + 1) + h);
+    if (n < 15) {
+      const int s1 = (n + 1) >> 2, t1 = (n + 1) & 3;
+      fast_decode_step<FM, FN>(ca[s1 & 1], cb[s1 & 1], sa, sb, s1, t1, av[(n + 1) & 1], bv[(n + 1) & 1]);
     }
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
-      const int row = wn * (32 * FN) + 32 * j + r;
-      cb[j] = *reinterpret_cast<const uint4*>(S.b_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
-      sb[j] = fast_scale_pair(S.b_scales, row, q);
-    }
+    for (int j = 0; j < FN; j++)
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      f16x8 av[FM], bv[FN];
-#pragma unroll
-      for (int i = 0; i < FM; i++) {
-        const f16x2 s2 = __builtin_bit_cast(f16x2, sa[i]);
-        const _Float16 sc = t < 2 ? s2.x : s2.y;
-        av[i] = decode8(word_of(ca[i], t), f16x2{sc, sc});
-      }
-#pragma unroll
-      for (int j = 0; j < FN; j++) {
-        const f16x2 s2 = __builtin_bit_cast(f16x2, sb[j]);
-        const _Float16 sc = t < 2 ? s2.x : s2.y;
-        bv[j] = decode8(word_of(cb[j], t), f16x2{sc, sc});
-      }
-#pragma unroll
-      for (int j = 0; j < FN; j++)
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[j][i], 0, 0, 0);
-    }
+      for (int i = 0; i < FM; i++)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[n & 1][j], av[n & 1][i], acc[j][i], 0, 0, 0);
   }
 }
 
