@@ -206,7 +206,7 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     return res
 
 
-def cpu_baseline(workloads, M, N, K, rows=1024):
+def cpu_baseline(workloads, M, N, K, rows=8192):
     """The CPU oracle (test infrastructure) on a bounded sample of the step:
     quantize `rows` activation rows with the tensor's s_g and compute their
     reference GEMM rows against all N weight rows (weights quantized once,

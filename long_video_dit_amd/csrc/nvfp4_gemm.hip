@@ -322,7 +322,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // outputs so that the compiler does not track these LDS writes (its tracking
 // falls back to waiting for every outstanding copy before any LDS read, which
 // would serialize the prefetch); completion is enforced explicitly with
-// s_waitcnt vmcnt(0) + s_barrier before a stage is read.
+// s_waitcnt vmcnt(0) + s_barrier before a stage is read.  M0 is reserved by
+// the compiler, hence the warning pragma: the fast kernel contains no
+// compiler-generated use of M0 (tests/test_build_checks.py verifies this on
+// the generated assembly), so setting it here disturbs nothing.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, const void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
@@ -331,6 +336,7 @@ __device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, con
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
 }
+#pragma clang diagnostic pop
 
 constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code bytes per row
 

@@ -10,7 +10,7 @@
 //   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
 //   encode_kernel        pass 2: scale byte per 16, 8 codes per lane
-//   dequant_kernel       codes + scales -> bf16 / fp32
+//   dequant_kernel       codes + scales -> bf16 / fp32, 8 outputs per lane
 //
 // The amax partials live in the caller's codes buffer (it is at least 4 B
 // per 8 elements), which the encode pass overwrites afterwards; the calls
@@ -160,8 +160,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   }
 }
 
-// grid: (X, G).  One lane per 16-element block: 8 code bytes + 1 scale byte
-// -> 16 outputs.
 // val(code) of the two nibbles of byte S of w, times the block scale (exact).
 template <int S>
 __device__ __forceinline__ void decode_pair(uint32_t w, float sv, float* p) {
@@ -170,40 +168,36 @@ __device__ __forceinline__ void decode_pair(uint32_t w, float sv, float* p) {
   p[1] = d.y * sv;
 }
 
+// grid: (X, G).  One lane per 8-element unit (4 code bytes, the block's scale
+// byte) -> 8 outputs, so that every store instruction of a wave writes one
+// contiguous span (1 KiB of bf16).  Splitting a lane's output over two
+// strided 16-byte stores instead costs ~30% extra HBM write traffic.
 template <bool kBf16Out>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const u32x2* __restrict__ codes,
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
-                                                           int64_t blocks_per_group, const float* __restrict__ s_g,
+                                                           int64_t units_per_group, const float* __restrict__ s_g,
                                                            void* __restrict__ y) {
   const int g = blockIdx.y;
   const float sg = s_g[g];
-  const int64_t base = (int64_t)g * blocks_per_group;
+  const int64_t base = (int64_t)g * units_per_group;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < blocks_per_group; b += stride) {
-    const u32x2 w = __builtin_nontemporal_load(codes + base + b);
-    const float sv = e4m3_value(scales[base + b]);
-    float p[16];  // val(code) * val(scale), exact: <= 6 significant bits
-    decode_pair<0>(w.x, sv, p + 0);
-    decode_pair<1>(w.x, sv, p + 2);
-    decode_pair<2>(w.x, sv, p + 4);
-    decode_pair<3>(w.x, sv, p + 6);
-    decode_pair<0>(w.y, sv, p + 8);
-    decode_pair<1>(w.y, sv, p + 10);
-    decode_pair<2>(w.y, sv, p + 12);
-    decode_pair<3>(w.y, sv, p + 14);
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units_per_group; u += stride) {
+    const uint32_t w = __builtin_nontemporal_load(codes + base + u);
+    const float sv = e4m3_value(scales[(base + u) >> 1]);
+    float p[8];  // val(code) * val(scale), exact: <= 6 significant bits
+    decode_pair<0>(w, sv, p + 0);
+    decode_pair<1>(w, sv, p + 2);
+    decode_pair<2>(w, sv, p + 4);
+    decode_pair<3>(w, sv, p + 6);
     if constexpr (kBf16Out) {
-      uint32_t o[8];
+      uint32_t o[4];
 #pragma unroll
-      for (int i = 0; i < 8; i++) o[i] = bf16_of_product(p[2 * i], sg) | (bf16_of_product(p[2 * i + 1], sg) << 16);
-      u32x4* dst = reinterpret_cast<u32x4*>(y) + 2 * (base + b);
-      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst);
-      __builtin_nontemporal_store(u32x4{o[4], o[5], o[6], o[7]}, dst + 1);
+      for (int i = 0; i < 4; i++) o[i] = bf16_of_product(p[2 * i], sg) | (bf16_of_product(p[2 * i + 1], sg) << 16);
+      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(y) + (base + u));
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(y) + 4 * (base + b);
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        __builtin_nontemporal_store(f32x4{p[4 * q] * sg, p[4 * q + 1] * sg, p[4 * q + 2] * sg, p[4 * q + 3] * sg},
-                                    dst + q);
+      f32x4* dst = reinterpret_cast<f32x4*>(y) + 2 * (base + u);
+      __builtin_nontemporal_store(f32x4{p[0] * sg, p[1] * sg, p[2] * sg, p[3] * sg}, dst);
+      __builtin_nontemporal_store(f32x4{p[4] * sg, p[5] * sg, p[6] * sg, p[7] * sg}, dst + 1);
     }
   }
 }
@@ -256,14 +250,15 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
                           int groups, void* y, int y_dtype, hipStream_t stream) {
   if (blocks_per_group == 0) return hipSuccess;
+  const int64_t units = 2 * blocks_per_group;
   const int cus = device_cu_count();
-  const int bx = grid_blocks(blocks_per_group, 1, std::max(1, cus * 16 / groups));
+  const int bx = grid_blocks(units, 2, std::max(1, cus * 16 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (y_dtype == kDtypeF32)
-    return launch_kernel(dequant_kernel<false>, grid, dim3(kThreads), 0, stream, (const u32x2*)codes, scales,
-                         blocks_per_group, s_g, y);
-  return launch_kernel(dequant_kernel<true>, grid, dim3(kThreads), 0, stream, (const u32x2*)codes, scales,
-                       blocks_per_group, s_g, y);
+    return launch_kernel(dequant_kernel<false>, grid, dim3(kThreads), 0, stream, (const uint32_t*)codes, scales, units,
+                         s_g, y);
+  return launch_kernel(dequant_kernel<true>, grid, dim3(kThreads), 0, stream, (const uint32_t*)codes, scales, units,
+                       s_g, y);
 }
 
 }  // namespace nvfp4

@@ -1,0 +1,116 @@
+"""Host-side checks of the built library (no GPU needed): the C ABI exports
+every function include/nvfp4.h declares, argument validation rejects bad
+calls before any launch, and the GEMM fast path's generated gfx950 assembly
+leaves M0 to the direct-to-LDS copies alone."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _lib():
+    from long_video_dit_amd import nvfp4
+    return nvfp4.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status_t|int|const char \*)\s*(\w+)\(", text, re.M)))
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert set(names) >= {"nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_gemm_fused_act",
+                          "kv_quantize", "kv_dequantize", "nvfp4_abi_version", "nvfp4_status_string"}
+    lib = _lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\S+)", out))
+    assert set(names) <= exported
+
+
+def test_binding_signatures_cover_header():
+    from long_video_dit_amd import nvfp4
+    assert set(nvfp4.SIGNATURES) == set(_declared_functions())
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.nvfp4_abi_version() == 1
+    for st in range(7):
+        assert len(lib.nvfp4_status_string(st)) >= 2
+    assert lib.nvfp4_status_string(99) == b"unknown status"
+
+
+def test_validation_errors_launch_nothing():
+    """Every invalid-argument path returns its status before touching the GPU."""
+    from long_video_dit_amd import nvfp4 as nv
+    lib = _lib()
+    P = ctypes.c_void_p
+    buf = P(1 << 20)  # 16-byte aligned fake address: never dereferenced on these paths
+    odd = P((1 << 20) + 2)
+    # quantize
+    assert lib.nvfp4_quantize(buf, 7, 4, 32, buf, buf, buf, 0, None) == nv.ERR_DTYPE
+    assert lib.nvfp4_quantize(buf, 1, 4, 32, buf, buf, buf, 5, None) == nv.ERR_FLAGS
+    assert lib.nvfp4_quantize(buf, 1, 4, 24, buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_quantize(buf, 1, -1, 32, buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_quantize(buf, 1, 4, 0, buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_quantize(buf, 1, 1 << 30, 1 << 20, buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_quantize(None, 1, 4, 32, buf, buf, buf, 0, None) == nv.ERR_NULL
+    assert lib.nvfp4_quantize(buf, 1, 4, 32, buf, buf, None, 0, None) == nv.ERR_NULL
+    assert lib.nvfp4_quantize(odd, 1, 4, 32, buf, buf, buf, 0, None) == nv.ERR_ALIGN
+    # dequantize
+    assert lib.nvfp4_dequantize(buf, buf, buf, 4, 32, buf, 3, None) == nv.ERR_DTYPE
+    assert lib.nvfp4_dequantize(buf, buf, buf, 4, 40, buf, 1, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_dequantize(None, buf, buf, 4, 32, buf, 1, None) == nv.ERR_NULL
+    assert lib.nvfp4_dequantize(buf, buf, buf, 4, 32, odd, 1, None) == nv.ERR_ALIGN
+    # gemm
+    assert lib.nvfp4_gemm(buf, buf, buf, buf, buf, buf, 0, 8, 32, buf, 1, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_gemm(buf, buf, buf, buf, buf, buf, 8, 8, 24, buf, 1, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_gemm(buf, buf, buf, buf, buf, buf, 1 << 31, 8, 32, buf, 1, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_gemm(buf, buf, buf, buf, buf, buf, 8, 8, 32, buf, 9, None) == nv.ERR_DTYPE
+    assert lib.nvfp4_gemm(buf, None, buf, buf, buf, buf, 8, 8, 32, buf, 1, None) == nv.ERR_NULL
+    assert lib.nvfp4_gemm(buf, buf, buf, odd, buf, buf, 8, 8, 32, buf, 1, None) == nv.ERR_ALIGN
+    # fused activation linear
+    assert lib.nvfp4_gemm_fused_act(buf, 5, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_DTYPE
+    assert lib.nvfp4_gemm_fused_act(None, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_NULL
+    assert lib.nvfp4_gemm_fused_act(buf, 1, 8, 48 + 8, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_SHAPE
+    # KV cache
+    assert lib.kv_quantize(buf, 0, 16, 128, buf, buf, buf, None) == nv.ERR_SHAPE
+    assert lib.kv_quantize(buf, 4, 16, 120, buf, buf, buf, None) == nv.ERR_SHAPE
+    assert lib.kv_quantize(buf, 4, 16, 128, buf, buf, None, None) == nv.ERR_NULL
+    assert lib.kv_dequantize(buf, buf, buf, 4, -1, 128, buf, None) == nv.ERR_SHAPE
+    assert lib.kv_dequantize(buf, buf, buf, 4, 16, 128, odd, None) == nv.ERR_ALIGN
+
+
+def test_gemm_fast_path_leaves_m0_to_the_lds_copies():
+    """The fast GEMM kernel sets M0 inside its own asm statements; the compiler
+    must not keep any value of its own in M0 in that kernel."""
+    src = os.path.join(ROOT, "long_video_dit_amd", "csrc", "nvfp4_gemm.hip")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "gemm.s")
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-O3", "-std=c++17",
+                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", src, "-o", out],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.fail(r.stderr[-2000:])
+        asm = open(out).read()
+    kernels = re.findall(r"^(_Z\S*fast_kernel\S*):", asm, re.M)
+    assert kernels
+    for k in kernels:
+        body = asm[asm.index(k + ":"):asm.index(".Lfunc_end", asm.index(k + ":"))]
+        inside = False
+        for line in body.splitlines():
+            if ";;#ASMSTART" in line:
+                inside = True
+            elif ";;#ASMEND" in line:
+                inside = False
+            elif not inside:
+                assert not re.search(r"\bm0\b", line.split(";")[0]), (k, line)
