@@ -31,10 +31,6 @@
 #define NVFP4_GEMM_WM 2
 #define NVFP4_GEMM_WN 2
 #endif
-#ifndef NVFP4_GEMM_FAST_WM
-#define NVFP4_GEMM_FAST_WM 2
-#define NVFP4_GEMM_FAST_WN 2
-#endif
 
 namespace nvfp4 {
 
@@ -186,6 +182,18 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 sc) {
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int t) {
   return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+}
+
+// Linear tile index -> (tile_m, tile_n), grouped by kGroupM tile rows so
+// that consecutive indices share A rows and B rows.
+__device__ __forceinline__ void tile_of_lin(int lin, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int group = lin / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int in_group = lin % per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
 }
 
 // Workgroup id -> (tile_m, tile_n): XCD-contiguous, then grouped by 8 tile rows.
@@ -347,64 +355,83 @@ struct __attribute__((aligned(16))) FastStage {
   uint8_t b_scales[kTile * 16];
 };
 
-// Per-lane byte offsets (row clamped to the last valid row, plane slot
-// swizzle applied) of the copies one thread issues per stage; computed once
-// per tile.  Offsets are 32-bit: the fast path requires operands < 4 GiB.
-template <int W>
-struct FastOffsets {
-  static constexpr int kCodeInsts = 32 / W;  // 2048 pieces of 16 B per operand, 64 per instruction
-  static constexpr int kScaleInsts = 16 / W;  // 1024 dwords of scales per operand
-  uint32_t a[kCodeInsts], b[kCodeInsts], sa[kScaleInsts], sb[kScaleInsts];
+// Copies of one stage (K = 256 of a 256-row tile of A and of B) issued by one
+// thread: wave w fills rows 64 w .. 64 w + 63 of both operands, 8 rows (1 KiB
+// of codes) per 16-byte copy instruction and 16 rows of scale bytes per
+// 4-byte copy.  For a full tile the per-lane part of each source offset only
+// depends on the lane and on the instruction's parity (the plane swizzle
+// q ^ ((row / 2) % 8) repeats every 16 rows), so it is kept in 3 VGPRs and
+// the row advance goes into the uniform SGPR base.  Tiles that cross the
+// last row of A or B clamp every lane's row and take the per-lane path.
+struct FastLoad {
+  uint32_t vo[2];  // code offsets of even / odd instructions (full tiles)
+  uint32_t vs;     // scale offset (full tiles)
 };
 
-template <int W>
-__device__ __forceinline__ void fast_offsets(FastOffsets<W>& o, int64_t m0, int64_t n0, int M, int N, int K) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ FastLoad fast_load_offsets(int K) {
+  const int lane = threadIdx.x & 63;
   const uint32_t row_bytes = (uint32_t)(K / 2), srow_bytes = (uint32_t)(K / 16);
+  FastLoad o;
 #pragma unroll
-  for (int i = 0; i < FastOffsets<W>::kCodeInsts; i++) {
-    const int slot = (w * FastOffsets<W>::kCodeInsts + i) * 64 + lane;
-    const int row = slot >> 3;
-    const uint32_t q = (slot & 7) ^ ((row >> 1) & 7);
-    const uint32_t ra = (uint32_t)(m0 + row < M ? m0 + row : M - 1);
-    const uint32_t rb = (uint32_t)(n0 + row < N ? n0 + row : N - 1);
-    o.a[i] = ra * row_bytes + 16 * q;
-    o.b[i] = rb * row_bytes + 16 * q;
+  for (int p = 0; p < 2; p++) {
+    const int row = 8 * p + (lane >> 3);  // row within a 16-row period
+    const uint32_t q = (lane & 7) ^ ((row >> 1) & 7);
+    o.vo[p] = (uint32_t)(lane >> 3) * row_bytes + 16 * q;
   }
-#pragma unroll
-  for (int i = 0; i < FastOffsets<W>::kScaleInsts; i++) {
-    const int d = (w * FastOffsets<W>::kScaleInsts + i) * 64 + lane;
-    const int row = d >> 2;
-    const uint32_t dw = d & 3;
-    const uint32_t ra = (uint32_t)(m0 + row < M ? m0 + row : M - 1);
-    const uint32_t rb = (uint32_t)(n0 + row < N ? n0 + row : N - 1);
-    o.sa[i] = ra * srow_bytes + 4 * dw;
-    o.sb[i] = rb * srow_bytes + 4 * dw;
-  }
+  o.vs = (uint32_t)(lane >> 2) * srow_bytes + 4 * (lane & 3);
+  return o;
 }
 
-template <int W>
-__device__ __forceinline__ void fast_load_stage(FastStage& S, const FastOffsets<W>& o,
+__device__ __forceinline__ void fast_load_stage(FastStage& S, const FastLoad& o, bool edge,
                                                 const uint8_t* __restrict__ a_codes,
                                                 const uint8_t* __restrict__ a_scales,
                                                 const uint8_t* __restrict__ b_codes,
-                                                const uint8_t* __restrict__ b_scales, int kc) {
-  const int w = threadIdx.x >> 6;
-  const uint8_t* ac = a_codes + (size_t)kc * 128;
-  const uint8_t* bc = b_codes + (size_t)kc * 128;
-  const uint8_t* as = a_scales + (size_t)kc * 16;
-  const uint8_t* bs = b_scales + (size_t)kc * 16;
+                                                const uint8_t* __restrict__ b_scales, int64_t m0, int64_t n0, int M,
+                                                int N, int K, int kc) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t row_bytes = K / 2, srow_bytes = K / 16;
+  if (!edge) {
+    const uint8_t* ac = a_codes + (m0 + 64 * w) * row_bytes + kc * 128;
+    const uint8_t* bc = b_codes + (n0 + 64 * w) * row_bytes + kc * 128;
 #pragma unroll
-  for (int i = 0; i < FastOffsets<W>::kCodeInsts; i++) {
-    const int slot0 = (w * FastOffsets<W>::kCodeInsts + i) * 64;
-    lds_dma16(ac, o.a[i], S.a_codes + slot0 * 16);
-    lds_dma16(bc, o.b[i], S.b_codes + slot0 * 16);
+    for (int i = 0; i < 8; i++) {
+      const int slot0 = (w * 8 + i) * 64;
+      lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], S.a_codes + slot0 * 16);
+      lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], S.b_codes + slot0 * 16);
+    }
+    const uint8_t* as = a_scales + (m0 + 64 * w) * srow_bytes + kc * 16;
+    const uint8_t* bs = b_scales + (n0 + 64 * w) * srow_bytes + kc * 16;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int d0 = (w * 4 + i) * 64;
+      lds_dma4(as + 16 * i * srow_bytes, o.vs, S.a_scales + d0 * 4);
+      lds_dma4(bs + 16 * i * srow_bytes, o.vs, S.b_scales + d0 * 4);
+    }
+    return;
   }
+  const uint8_t* ac = a_codes + kc * 128;
+  const uint8_t* bc = b_codes + kc * 128;
 #pragma unroll
-  for (int i = 0; i < FastOffsets<W>::kScaleInsts; i++) {
-    const int d0 = (w * FastOffsets<W>::kScaleInsts + i) * 64;
-    lds_dma4(as, o.sa[i], S.a_scales + d0 * 4);
-    lds_dma4(bs, o.sb[i], S.b_scales + d0 * 4);
+  for (int i = 0; i < 8; i++) {
+    const int slot0 = (w * 8 + i) * 64;
+    const int row = (slot0 + lane) >> 3;
+    const uint32_t q = ((slot0 + lane) & 7) ^ ((row >> 1) & 7);
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, S.a_codes + slot0 * 16);
+    lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, S.b_codes + slot0 * 16);
+  }
+  const uint8_t* as = a_scales + kc * 16;
+  const uint8_t* bs = b_scales + kc * 16;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int d0 = (w * 4 + i) * 64;
+    const int row = (d0 + lane) >> 2;
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    lds_dma4(as, (uint32_t)(ra * srow_bytes) + 4 * (lane & 3), S.a_scales + d0 * 4);
+    lds_dma4(bs, (uint32_t)(rb * srow_bytes) + 4 * (lane & 3), S.b_scales + d0 * 4);
   }
 }
 
@@ -454,12 +481,63 @@ __device__ __forceinline__ void fast_decode_step(const uint4 (&ca)[FM], const ui
   }
 }
 
+// One quarter of a k16-step, hand-interleaved: 4 MFMAs (output tiles (j, 0..3)
+// of B frag j against the 4 A frags) with 4 decode VALU instructions after
+// each, which decode two frags (x, y) of the NEXT k16-step (4 conversions +
+// 4 fp16 scale multiplies each).  The compiler schedules MFMAs back to back
+// and the decode work in long runs, so a wave (one per SIMD) alternates
+// between an idle matrix core and an idle VALU; this keeps both busy.  `hi`
+// selects which fp16 of the scale pair applies (blocks 2q / 2q + 1).
+// Register hazards: the decoded outputs are next-step buffers whose last MFMA
+// readers were issued at least one MFMA (32 cycles) earlier, and every output
+// is first read by an MFMA at least one block later; each block starts with
+// s_nop for the VALU-write -> MFMA-read distance across blocks.
+#define NVFP4_DEC_PAIR(O, W, S, SEL, OPS)                                          \
+  "v_cvt_scalef32_pk_f16_fp4 %[" O "], %[" W "], 1.0" SEL "\n\t"                  \
+  "v_pk_mul_f16 %[" O "], %[" S "], %[" O "]" OPS "\n\t"
+#define NVFP4_DEC_FRAG(P, W, S, OPS)                                               \
+  NVFP4_DEC_PAIR(P "0", W, S, "", OPS) NVFP4_DEC_PAIR(P "1", W, S, " op_sel:[1,0,0]", OPS) \
+  NVFP4_DEC_PAIR(P "2", W, S, " op_sel:[0,1,0]", OPS) NVFP4_DEC_PAIR(P "3", W, S, " op_sel:[1,1,0]", OPS)
+#define NVFP4_MFMA(C) "v_mfma_f32_32x32x16_f16 %[" C "], %[b], %[a" C "], %[" C "]\n\t"
+
+template <bool kHi>
+__device__ __forceinline__ void mfma4_decode2(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const f16x8& b,
+                                              const f16x8 (&a)[4], uint32_t wx, uint32_t sx, uint32_t wy,
+                                              uint32_t sy, f16x8& ox, f16x8& oy) {
+  uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
+#define NVFP4_BODY(OPS)                                                                              \
+  "s_nop 1\n\t" NVFP4_MFMA("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                           \
+      NVFP4_DEC_PAIR("x1", "wx", "sx", " op_sel:[1,0,0]", OPS) NVFP4_MFMA("c1")                      \
+      NVFP4_DEC_PAIR("x2", "wx", "sx", " op_sel:[0,1,0]", OPS)                                       \
+      NVFP4_DEC_PAIR("x3", "wx", "sx", " op_sel:[1,1,0]", OPS) NVFP4_MFMA("c2")                      \
+      NVFP4_DEC_PAIR("y0", "wy", "sy", "", OPS) NVFP4_DEC_PAIR("y1", "wy", "sy", " op_sel:[1,0,0]", OPS) \
+      NVFP4_MFMA("c3") NVFP4_DEC_PAIR("y2", "wy", "sy", " op_sel:[0,1,0]", OPS)                      \
+      NVFP4_DEC_PAIR("y3", "wy", "sy", " op_sel:[1,1,0]", OPS)
+  if constexpr (kHi) {
+    asm volatile(NVFP4_BODY(" op_sel:[1,0] op_sel_hi:[1,1]")
+                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
+                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3)
+                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
+                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy));
+  } else {
+    asm volatile(NVFP4_BODY(" op_sel:[0,0] op_sel_hi:[0,1]")
+                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
+                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3)
+                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
+                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy));
+  }
+#undef NVFP4_BODY
+  ox = __builtin_bit_cast(f16x8, u32x4{x0, x1, x2, x3});
+  oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
+}
+
 // One stage (K = 256 = 4 sub-chunks x 4 k16-steps), software-pipelined: the
 // codes of sub-chunk s + 1 are read while sub-chunk s is multiplied, and
-// k16-step n + 1 is decoded while the MFMAs of step n run.
-template <int FM, int FN>
-__device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&acc)[FN][FM], int wm, int wn, int r,
+// k16-step n + 1 is decoded (inside the interleaved MFMA blocks) while the
+// MFMAs of step n run.  Wave layout 2 x 2 (FM = FN = 4).
+__device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&acc)[4][4], int wm, int wn, int r,
                                                    int h) {
+  constexpr int FM = 4, FN = 4;
   uint32_t sa[FM][4], sb[FN][4];
 #pragma unroll
   for (int i = 0; i < FM; i++) fast_scale_pairs(S.a_scales, wm * (32 * FM) + 32 * i + r, h, sa[i]);
@@ -473,70 +551,47 @@ __device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&
   for (int n = 0; n < 16; n++) {
     const int s = n >> 2, t = n & 3;
     if (t == 0 && s < 3) fast_read_codes<FM, FN>(S, ca[(s + 1) & 1], cb[(s + 1) & 1], wm, wn, r, 2 * (s + 1) + h);
+    const int c = n & 1, x = (n + 1) & 1;
     if (n < 15) {
       const int s1 = (n + 1) >> 2, t1 = (n + 1) & 3;
-      fast_decode_step<FM, FN>(ca[s1 & 1], cb[s1 & 1], sa, sb, s1, t1, av[(n + 1) & 1], bv[(n + 1) & 1]);
+      const uint4* A = ca[s1 & 1];
+      const uint4* B = cb[s1 & 1];
+      // blocks 0-1 decode the next step's A frags, blocks 2-3 its B frags
+#define NVFP4_Q(J, W0, S0, W1, S1, O0, O1)                                                                  \
+  if (t1 < 2)                                                                                             \
+    mfma4_decode2<false>(acc[J][0], acc[J][1], acc[J][2], acc[J][3], bv[c][J], av[c], W0, S0, W1, S1, O0, O1); \
+  else                                                                                                    \
+    mfma4_decode2<true>(acc[J][0], acc[J][1], acc[J][2], acc[J][3], bv[c][J], av[c], W0, S0, W1, S1, O0, O1);
+      NVFP4_Q(0, word_of(A[0], t1), sa[0][s1], word_of(A[1], t1), sa[1][s1], av[x][0], av[x][1])
+      NVFP4_Q(1, word_of(A[2], t1), sa[2][s1], word_of(A[3], t1), sa[3][s1], av[x][2], av[x][3])
+      NVFP4_Q(2, word_of(B[0], t1), sb[0][s1], word_of(B[1], t1), sb[1][s1], bv[x][0], bv[x][1])
+      NVFP4_Q(3, word_of(B[2], t1), sb[2][s1], word_of(B[3], t1), sb[3][s1], bv[x][2], bv[x][3])
+#undef NVFP4_Q
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[c][j], av[c][i], acc[j][i], 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < FN; j++)
-#pragma unroll
-      for (int i = 0; i < FM; i++)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[n & 1][j], av[n & 1][i], acc[j][i], 0, 0, 0);
   }
 }
 
-template <int WM, int WN, bool kBf16Out>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_fast_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
-    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const float* __restrict__ b_sg, int M,
-    int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
-  constexpr int W = WM * WN;
-  constexpr int FM = kTile / (32 * WM), FN = kTile / (32 * WN);
-  __shared__ FastStage st0;
-  __shared__ FastStage st1;
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  const int nk = K / kFastKC;  // even
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int r = lane & 31, h = lane >> 5;
-
-  f32x16 acc[FN][FM];
+// Epilogue of one tile: lane (r, h), accumulator element e of MFMA tile (j, i)
+// is output row m = 32 i + r and column n = 32 j + 8 (e / 4) + 4 h + e % 4;
+// one 8-byte (bf16) or 16-byte (fp32) store per 4 consecutive columns.
+template <bool kBf16Out>
+__device__ __forceinline__ void fast_epilogue(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0, int64_t n0,
+                                              int M, int N, int wm, int wn, int r, int h, float g) {
 #pragma unroll
-  for (int j = 0; j < FN; j++)
-#pragma unroll
-    for (int i = 0; i < FM; i++) acc[j][i] = f32x16{};
-
-  FastOffsets<W> off;
-  fast_offsets<W>(off, m0, n0, M, N, K);
-  fast_load_stage<W>(st0, off, a_codes, a_scales, b_codes, b_scales, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; kc += 2) {
-    fast_load_stage<W>(st1, off, a_codes, a_scales, b_codes, b_scales, kc + 1);
-    fast_compute_stage<FM, FN>(st0, acc, wm, wn, r, h);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kc + 2 < nk) fast_load_stage<W>(st0, off, a_codes, a_scales, b_codes, b_scales, kc + 2);
-    fast_compute_stage<FM, FN>(st1, acc, wm, wn, r, h);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  // Epilogue: lane (r, h), accumulator element e of tile (j, i) is output row
-  // m = 32 i + r and column n = 32 j + 8 (e / 4) + 4 h + e % 4.
-  const float g = a_sg[0] * b_sg[0];
-#pragma unroll
-  for (int i = 0; i < FM; i++) {
-    const int64_t m = m0 + wm * (32 * FM) + 32 * i + r;
+  for (int i = 0; i < 4; i++) {
+    const int64_t m = m0 + wm * 128 + 32 * i + r;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
+    for (int j = 0; j < 4; j++) {
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) {
-        const int64_t n = n0 + wn * (32 * FN) + 32 * j + 8 * gq + 4 * h;
+        const int64_t n = n0 + wn * 128 + 32 * j + 8 * gq + 4 * h;
         if (n >= N) continue;  // N % 4 == 0: the 4 columns are all in or all out
         const float v0 = acc[j][i][4 * gq] * g, v1 = acc[j][i][4 * gq + 1] * g;
         const float v2 = acc[j][i][4 * gq + 2] * g, v3 = acc[j][i][4 * gq + 3] * g;
@@ -549,6 +604,71 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_fast_kernel(
         }
       }
     }
+  }
+}
+
+// Persistent fast-path kernel: one workgroup per CU walks tiles lin, lin + G,
+// lin + 2G, ... (G = grid size).  Workgroups are dealt round-robin to the 8
+// XCDs, so lin is remapped to keep the tiles processed concurrently by one
+// XCD contiguous (they then share A and B rows in that XCD's L2).  Between
+// tiles the first stage of the next tile is fetched while the previous
+// tile's results are being stored, so neither the store drain, the workgroup
+// turnover nor the first fetch stalls the matrix cores.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const float* __restrict__ b_sg, int M,
+    int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
+  __shared__ FastStage st0;
+  __shared__ FastStage st1;
+  const int T = tiles_m * tiles_n;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int lin0 = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+  const int nk = K / kFastKC;  // even
+  const float g = a_sg[0] * b_sg[0];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, h = lane >> 5;
+
+  const FastLoad ld = fast_load_offsets(K);
+  int tm, tn;
+  tile_of_lin(lin0, tiles_m, tiles_n, tm, tn);
+  bool edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTile > N;
+  fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
+                  K, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int lin = lin0; lin < T; lin += G) {
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[j][i] = f32x16{};
+    for (int kc = 0; kc < nk; kc += 2) {
+      fast_load_stage(st1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 1);
+      fast_compute_stage(st0, acc, wm, wn, r, h);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kc + 2 < nk) fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+      fast_compute_stage(st1, acc, wm, wn, r, h);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    // Prefetch the first stage of the next tile into st0 (free: its last
+    // reader finished before the barrier above), then store this tile.
+    if (lin + G < T) {
+      tile_of_lin(lin + G, tiles_m, tiles_n, tm, tn);
+      edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTile > N;
+      fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile,
+                      M, N, K, 0);
+    }
+    fast_epilogue<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 }
 
@@ -568,13 +688,14 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                    ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 4 == 0) &&
                    ((uintptr_t)b_scales % 4 == 0) && ((uintptr_t)c % 16 == 0);
   if (dma) {
-    constexpr int FWM = NVFP4_GEMM_FAST_WM, FWN = NVFP4_GEMM_FAST_WN;
-    const dim3 fblock(64 * FWM * FWN);
+    const int T = tiles_m * tiles_n;
+    const int cus = device_cu_count();
+    const dim3 pgrid((unsigned)(T < cus ? T : cus));
     if (bf)
-      return launch_kernel(gemm_w4a4_fast_kernel<FWM, FWN, true>, grid, fblock, 0, stream, a_codes, a_scales, a_sg,
-                           b_codes, b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
-    return launch_kernel(gemm_w4a4_fast_kernel<FWM, FWN, false>, grid, fblock, 0, stream, a_codes, a_scales, a_sg,
-                         b_codes, b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
+      return launch_kernel(gemm_w4a4_fast_kernel<true>, pgrid, dim3(256), 0, stream, a_codes, a_scales, a_sg, b_codes,
+                           b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
+    return launch_kernel(gemm_w4a4_fast_kernel<false>, pgrid, dim3(256), 0, stream, a_codes, a_scales, a_sg, b_codes,
+                         b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
   }
 #define NVFP4_GEMM_LAUNCH(F, B)                                                                      \
   launch_kernel(gemm_w4a4_kernel<WM, WN, F, B>, grid, block, 0, stream, a_codes, a_scales, a_sg, b_codes, \

@@ -105,3 +105,22 @@ def test_gemm_deterministic():
     a = nv.quantize(_rand((1024, 1024), 1).to(dev()))
     b = nv.quantize(_rand((768, 1024), 2).to(dev()))
     assert torch.equal(nv.gemm(a, b), nv.gemm(a, b))
+
+
+def test_gemm_many_tiles_with_ragged_edges():
+    """More tiles than workgroups (each walks several tiles), last tile row and
+    column ragged; sampled rows and columns against the oracle."""
+    nv = _nv()
+    M, N, K = 16 * 256 + 100, 17 * 256 - 60, 512
+    log("gemm many tiles", M, N, K)
+    a = _rand((M, K), 11)
+    b = _rand((N, K), 12)
+    aq, bq = nv.quantize(a.to(dev())), nv.quantize(b.to(dev()))
+    c = c_to_f64(nv.gemm(aq, bq, out_dtype=torch.bfloat16))
+    ao, bo = oracle.quantize(oracle_input(a)), oracle.quantize(oracle_input(b))
+    rows = np.array([0, 255, 256, 4095, 4096, 4150, M - 1])
+    cols = np.array([0, 3, 255, 256, 4095, 4096, N - 4, N - 1])
+    ref, tot = oracle.gemm_ref(*ao, *bo, rows=rows)
+    check_gemm_bound(c[rows], ref, tot, True, "many tiles rows")
+    ref, tot = oracle.gemm_ref(*ao, *bo, cols=cols)
+    check_gemm_bound(c[:, cols], ref, tot, True, "many tiles cols")
