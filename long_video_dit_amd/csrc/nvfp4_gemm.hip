@@ -610,10 +610,10 @@ __device__ __forceinline__ void fast_epilogue(const f32x16 (&acc)[4][4], void* _
 // Persistent fast-path kernel: one workgroup per CU walks tiles lin, lin + G,
 // lin + 2G, ... (G = grid size).  Workgroups are dealt round-robin to the 8
 // XCDs, so lin is remapped to keep the tiles processed concurrently by one
-// XCD contiguous (they then share A and B rows in that XCD's L2).  Between
-// tiles the first stage of the next tile is fetched while the previous
-// tile's results are being stored, so neither the store drain, the workgroup
-// turnover nor the first fetch stalls the matrix cores.
+// XCD contiguous (they then share A and B rows in that XCD's L2).  The first
+// stage of the next tile is fetched during the last stage of the current one
+// and the epilogue stores are not waited for, so neither the store drain,
+// the workgroup turnover nor the first fetch stalls the matrix cores.
 template <bool kBf16Out>
 __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
@@ -643,6 +643,10 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
 
   for (int lin = lin0; lin < T; lin += G) {
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    const bool has_next = lin + G < T;
+    int tm_next = tm, tn_next = tn;
+    if (has_next) tile_of_lin(lin + G, tiles_m, tiles_n, tm_next, tn_next);
+    const bool edge_next = (int64_t)(tm_next + 1) * kTile > M || (int64_t)(tn_next + 1) * kTile > N;
     f32x16 acc[4][4];
 #pragma unroll
     for (int j = 0; j < 4; j++)
@@ -653,22 +657,24 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
       fast_compute_stage(st0, acc, wm, wn, r, h);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (kc + 2 < nk) fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+      // st0 is free: fetch the next stage of this tile, or during the last
+      // stage the first stage of the next tile, so that it is complete at the
+      // barrier below and the epilogue stores never have to be waited for.
+      if (kc + 2 < nk)
+        fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+      else if (has_next)
+        fast_load_stage(st0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, (int64_t)tm_next * kTile,
+                        (int64_t)tn_next * kTile, M, N, K, 0);
       fast_compute_stage(st1, acc, wm, wn, r, h);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    // Prefetch the first stage of the next tile into st0 (free: its last
-    // reader finished before the barrier above), then store this tile.
-    if (lin + G < T) {
-      tile_of_lin(lin + G, tiles_m, tiles_n, tm, tn);
-      edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTile > N;
-      fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile,
-                      M, N, K, 0);
-    }
+    // The stores drain while the next tile computes (its first s_waitcnt comes
+    // a whole stage later).
     fast_epilogue<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    tm = tm_next;
+    tn = tn_next;
+    edge = edge_next;
   }
 }
 
