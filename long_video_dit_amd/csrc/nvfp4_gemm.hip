@@ -316,17 +316,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_kernel(
 // Per stage and operand: codes [256 rows][8 slots of 16 B] (256 codes per
 // row) with slot = plane q ^ ((row / 2) % 8), which makes both the 128 B
 // per-row coalesced fills and the 16-row operand reads bank-conflict free;
-// raw scale bytes [256 rows][16 B], read as one 16-byte vector per row and
-// stage and turned into fp16 pairs.  The MFMA takes B as its
-// first operand, so every lane ends with 4 consecutive output columns of one
-// row and the epilogue stores 8 (bf16) or 16 (fp32) bytes per instruction.
-// Rows past M or N are clamped to the last row: they only feed outputs that
-// are never stored.
+// raw scale bytes [256 rows][16 B].  The MFMA takes B as its first operand,
+// so every lane ends with 4 consecutive output columns of one row and the
+// epilogue stores 8 (bf16) or 16 (fp32) bytes per instruction.  Rows past M
+// or N are clamped to the last row: they only feed outputs that are never
+// stored.
+//
+// The k16-steps of all stages and tiles of a workgroup form one software
+// pipeline: each step's MFMAs run interleaved with the decode of the next
+// step, also across stage and tile boundaries, so no stage starts with a
+// decode or a scale conversion that the matrix cores would wait for.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // global -> LDS copy of 16 (or 4) bytes per lane: lane i reads base +
-// voff[i] and writes LDS address lds_base + 16 i (or 4 i); lds_base and base
-// are wave-uniform (M0 and an SGPR pair).  Issued as asm statements without
+// voff[i] and writes LDS address lds + 16 i (or 4 i); lds and base are
+// wave-uniform (M0 and an SGPR pair).  Issued as asm statements without
 // outputs so that the compiler does not track these LDS writes (its tracking
 // falls back to waiting for every outstanding copy before any LDS read, which
 // would serialize the prefetch); completion is enforced explicitly with
@@ -336,13 +340,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // the generated assembly), so setting it here disturbs nothing.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
 }
-__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff), "s"(base) : "m0");
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -354,6 +356,8 @@ struct __attribute__((aligned(16))) FastStage {
   uint8_t a_scales[kTile * 16];  // [row][16 scale bytes]
   uint8_t b_scales[kTile * 16];
 };
+// LDS byte offsets of the parts of a stage.
+constexpr uint32_t kStA = 0, kStB = kTile * 128, kStSA = 2 * kTile * 128, kStSB = 2 * kTile * 128 + kTile * 16;
 
 // Copies of one stage (K = 256 of a 256-row tile of A and of B) issued by one
 // thread: wave w fills rows 64 w .. 64 w + 63 of both operands, 8 rows (1 KiB
@@ -382,7 +386,8 @@ __device__ __forceinline__ FastLoad fast_load_offsets(int K) {
   return o;
 }
 
-__device__ __forceinline__ void fast_load_stage(FastStage& S, const FastLoad& o, bool edge,
+// Stage kc of the tile at rows (m0, n0) -> the LDS stage at address `lds`.
+__device__ __forceinline__ void fast_load_stage(uint32_t lds, const FastLoad& o, bool edge,
                                                 const uint8_t* __restrict__ a_codes,
                                                 const uint8_t* __restrict__ a_scales,
                                                 const uint8_t* __restrict__ b_codes,
@@ -396,17 +401,17 @@ __device__ __forceinline__ void fast_load_stage(FastStage& S, const FastLoad& o,
     const uint8_t* bc = b_codes + (n0 + 64 * w) * row_bytes + kc * 128;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const int slot0 = (w * 8 + i) * 64;
-      lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], S.a_codes + slot0 * 16);
-      lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], S.b_codes + slot0 * 16);
+      const uint32_t slot0 = (uint32_t)(w * 8 + i) * 64;
+      lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], lds + kStA + slot0 * 16);
+      lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], lds + kStB + slot0 * 16);
     }
     const uint8_t* as = a_scales + (m0 + 64 * w) * srow_bytes + kc * 16;
     const uint8_t* bs = b_scales + (n0 + 64 * w) * srow_bytes + kc * 16;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int d0 = (w * 4 + i) * 64;
-      lds_dma4(as + 16 * i * srow_bytes, o.vs, S.a_scales + d0 * 4);
-      lds_dma4(bs + 16 * i * srow_bytes, o.vs, S.b_scales + d0 * 4);
+      const uint32_t d0 = (uint32_t)(w * 4 + i) * 64;
+      lds_dma4(as + 16 * i * srow_bytes, o.vs, lds + kStSA + d0 * 4);
+      lds_dma4(bs + 16 * i * srow_bytes, o.vs, lds + kStSB + d0 * 4);
     }
     return;
   }
@@ -419,8 +424,8 @@ __device__ __forceinline__ void fast_load_stage(FastStage& S, const FastLoad& o,
     const uint32_t q = ((slot0 + lane) & 7) ^ ((row >> 1) & 7);
     const int64_t ra = m0 + row < M ? m0 + row : M - 1;
     const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-    lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, S.a_codes + slot0 * 16);
-    lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, S.b_codes + slot0 * 16);
+    lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, lds + kStA + (uint32_t)slot0 * 16);
+    lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, lds + kStB + (uint32_t)slot0 * 16);
   }
   const uint8_t* as = a_scales + kc * 16;
   const uint8_t* bs = b_scales + kc * 16;
@@ -430,54 +435,73 @@ __device__ __forceinline__ void fast_load_stage(FastStage& S, const FastLoad& o,
     const int row = (d0 + lane) >> 2;
     const int64_t ra = m0 + row < M ? m0 + row : M - 1;
     const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-    lds_dma4(as, (uint32_t)(ra * srow_bytes) + 4 * (lane & 3), S.a_scales + d0 * 4);
-    lds_dma4(bs, (uint32_t)(rb * srow_bytes) + 4 * (lane & 3), S.b_scales + d0 * 4);
+    lds_dma4(as, (uint32_t)(ra * srow_bytes) + 4 * (lane & 3), lds + kStSA + (uint32_t)d0 * 4);
+    lds_dma4(bs, (uint32_t)(rb * srow_bytes) + 4 * (lane & 3), lds + kStSB + (uint32_t)d0 * 4);
   }
 }
 
-// The 16 scale bytes of a row (one stage) -> the fp16 scale pairs of the 4
-// planes q = 2 s + h this lane uses (blocks 2q, 2q+1 in dword s, half h).
-__device__ __forceinline__ void fast_scale_pairs(const uint8_t* scales, int row, int h, uint32_t (&p)[4]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(scales + row * 16);
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+// Registers that carry the pipeline from step to step: the packed codes and
+// fp16 scale pairs of two sub-chunks (sub-chunk s of a stage uses buffer
+// s % 2) and the decoded MFMA operands of two k16-steps (step parity).
+struct FastPipe {
+  uint4 ca[2][4], cb[2][4];
+  uint32_t sa[2][4], sb[2][4];
+  f16x8 av[2][4], bv[2][4];
+};
+
+// Per-lane LDS offsets of the operand reads: lane (r, h) of wave (wm, wn)
+// reads rows wm * 128 + 32 i + r of A and wn * 128 + 32 j + r of B; within
+// a row, code plane q sits in slot q ^ sw with sw = (r / 2) % 8 (the same
+// for all 4 rows, which are 4 KiB apart), and the scale bytes of blocks 2q,
+// 2q + 1 at byte 2q.
+struct FastLane {
+  uint32_t a, b;    // code row offsets (row * 128) of row i = 0
+  uint32_t sa, sb;  // scale byte offsets (row * 16 + 2 h) of row i = 0
+  uint32_t hsw;     // 16 * (h ^ sw): slot offset of plane q = 2 s + h is hsw ^ (32 s)
+};
+
+// Sub-chunk s (K = 64 s .. 64 s + 63 of a stage) of LDS stage S -> buffer u:
+// this lane's 16 code bytes of plane q = 2 s + h of its 4 A rows and 4 B rows
+// (one 16-byte read each) and the 2 scale bytes of blocks 2q, 2q + 1 of each
+// row, left raw: fast_convert_scales turns them into fp16 once the reads
+// have landed.  The row offsets pass through an empty asm statement so that
+// the compiler derives each address here instead of keeping all of them
+// (2 stages x 4 sub-chunks x 8 rows) live in registers.
+__device__ __forceinline__ void fast_read_sub(const FastStage& S, FastPipe& P, int u, const FastLane& L, int s) {
+  uint32_t la = L.a, lb = L.b, lsa = L.sa, lsb = L.sb;
+  asm volatile("" : "+v"(la), "+v"(lb), "+v"(lsa), "+v"(lsb));
+  const uint32_t slot = L.hsw ^ (32u * s);
+  const uint8_t* ac = S.a_codes + (la + slot);
+  const uint8_t* bc = S.b_codes + (lb + slot);
+  const uint8_t* as = S.a_scales + (lsa + 4 * s);
+  const uint8_t* bs = S.b_scales + (lsb + 4 * s);
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const uint32_t b2 = d[s] >> (16 * h);
-    p[s] = e4m3x2_to_f16x2(b2 & 0xffu, (b2 >> 8) & 0xffu);
+  for (int i = 0; i < 4; i++) {
+    P.ca[u][i] = *reinterpret_cast<const uint4*>(ac + 4096 * i);
+    P.sa[u][i] = *reinterpret_cast<const uint16_t*>(as + 512 * i);
+    P.cb[u][i] = *reinterpret_cast<const uint4*>(bc + 4096 * i);
+    P.sb[u][i] = *reinterpret_cast<const uint16_t*>(bs + 512 * i);
   }
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void fast_read_codes(const FastStage& S, uint4 (&ca)[FM], uint4 (&cb)[FN], int wm, int wn,
-                                                int r, int q) {
+// Two E4M3 scale bytes -> two fp16 with the hardware converter (scale 1.0).
+// Exact: every finite E4M3 value, subnormals and signed zero included, is an
+// fp16 value.
+__device__ __forceinline__ void fast_convert_scales(FastPipe& P, int u) {
 #pragma unroll
-  for (int i = 0; i < FM; i++) {
-    const int row = wm * (32 * FM) + 32 * i + r;
-    ca[i] = *reinterpret_cast<const uint4*>(S.a_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
-  }
-#pragma unroll
-  for (int j = 0; j < FN; j++) {
-    const int row = wn * (32 * FN) + 32 * j + r;
-    cb[j] = *reinterpret_cast<const uint4*>(S.b_codes + row * 128 + 16 * (q ^ ((row >> 1) & 7)));
+  for (int i = 0; i < 4; i++) {
+    P.sa[u][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P.sa[u][i], 1.0f, false));
+    P.sb[u][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P.sb[u][i], 1.0f, false));
   }
 }
 
-// Decode k16-step t of the sub-chunk held in (ca, cb) with its scale pairs.
-template <int FM, int FN>
-__device__ __forceinline__ void fast_decode_step(const uint4 (&ca)[FM], const uint4 (&cb)[FN],
-                                                 const uint32_t (&sa)[FM][4], const uint32_t (&sb)[FN][4], int s,
-                                                 int t, f16x8 (&av)[FM], f16x8 (&bv)[FN]) {
+// The first k16-step of a workgroup's pipeline (sub-chunk 0, word 0, blocks 2h).
+__device__ __forceinline__ void fast_decode_first(FastPipe& P) {
 #pragma unroll
-  for (int i = 0; i < FM; i++) {
-    const f16x2 s2 = __builtin_bit_cast(f16x2, sa[i][s]);
-    const _Float16 sc = t < 2 ? s2.x : s2.y;
-    av[i] = decode8(word_of(ca[i], t), f16x2{sc, sc});
-  }
-#pragma unroll
-  for (int j = 0; j < FN; j++) {
-    const f16x2 s2 = __builtin_bit_cast(f16x2, sb[j][s]);
-    const _Float16 sc = t < 2 ? s2.x : s2.y;
-    bv[j] = decode8(word_of(cb[j], t), f16x2{sc, sc});
+  for (int i = 0; i < 4; i++) {
+    const _Float16 sa = __builtin_bit_cast(f16x2, P.sa[0][i]).x, sb = __builtin_bit_cast(f16x2, P.sb[0][i]).x;
+    P.av[0][i] = decode8(P.ca[0][i].x, f16x2{sa, sa});
+    P.bv[0][i] = decode8(P.cb[0][i].x, f16x2{sb, sb});
   }
 }
 
@@ -531,50 +555,66 @@ __device__ __forceinline__ void mfma4_decode2(f32x16& c0, f32x16& c1, f32x16& c2
   oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
 }
 
-// One stage (K = 256 = 4 sub-chunks x 4 k16-steps), software-pipelined: the
-// codes of sub-chunk s + 1 are read while sub-chunk s is multiplied, and
-// k16-step n + 1 is decoded (inside the interleaved MFMA blocks) while the
-// MFMAs of step n run.  Wave layout 2 x 2 (FM = FN = 4).
-__device__ __forceinline__ void fast_compute_stage(const FastStage& S, f32x16 (&acc)[4][4], int wm, int wn, int r,
-                                                   int h) {
-  constexpr int FM = 4, FN = 4;
-  uint32_t sa[FM][4], sb[FN][4];
-#pragma unroll
-  for (int i = 0; i < FM; i++) fast_scale_pairs(S.a_scales, wm * (32 * FM) + 32 * i + r, h, sa[i]);
-#pragma unroll
-  for (int j = 0; j < FN; j++) fast_scale_pairs(S.b_scales, wn * (32 * FN) + 32 * j + r, h, sb[j]);
-  uint4 ca[2][FM], cb[2][FN];
-  f16x8 av[2][FM], bv[2][FN];
-  fast_read_codes<FM, FN>(S, ca[0], cb[0], wm, wn, r, h);
-  fast_decode_step<FM, FN>(ca[0], cb[0], sa, sb, 0, 0, av[0], bv[0]);
-#pragma unroll
-  for (int n = 0; n < 16; n++) {
-    const int s = n >> 2, t = n & 3;
-    if (t == 0 && s < 3) fast_read_codes<FM, FN>(S, ca[(s + 1) & 1], cb[(s + 1) & 1], wm, wn, r, 2 * (s + 1) + h);
-    const int c = n & 1, x = (n + 1) & 1;
-    if (n < 15) {
-      const int s1 = (n + 1) >> 2, t1 = (n + 1) & 3;
-      const uint4* A = ca[s1 & 1];
-      const uint4* B = cb[s1 & 1];
-      // blocks 0-1 decode the next step's A frags, blocks 2-3 its B frags
-#define NVFP4_Q(J, W0, S0, W1, S1, O0, O1)                                                                  \
-  if (t1 < 2)                                                                                             \
-    mfma4_decode2<false>(acc[J][0], acc[J][1], acc[J][2], acc[J][3], bv[c][J], av[c], W0, S0, W1, S1, O0, O1); \
-  else                                                                                                    \
-    mfma4_decode2<true>(acc[J][0], acc[J][1], acc[J][2], acc[J][3], bv[c][J], av[c], W0, S0, W1, S1, O0, O1);
-      NVFP4_Q(0, word_of(A[0], t1), sa[0][s1], word_of(A[1], t1), sa[1][s1], av[x][0], av[x][1])
-      NVFP4_Q(1, word_of(A[2], t1), sa[2][s1], word_of(A[3], t1), sa[3][s1], av[x][2], av[x][3])
-      NVFP4_Q(2, word_of(B[0], t1), sb[0][s1], word_of(B[1], t1), sb[1][s1], bv[x][0], bv[x][1])
-      NVFP4_Q(3, word_of(B[2], t1), sb[2][s1], word_of(B[3], t1), sb[3][s1], bv[x][2], bv[x][3])
-#undef NVFP4_Q
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; j++)
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[c][j], av[c][i], acc[j][i], 0, 0, 0);
-    }
+// k16-step n of a stage read from LDS stage S: the codes and scales of
+// sub-chunk s + 1 are read at step 4 s and converted at step 4 s + 2; the
+// step's 16 MFMAs (operands decoded one step earlier) carry the decode of
+// step n + 1, which for n = 15 is the first step of the next stage (its
+// sub-chunk 0 is read in buffer 0 at step 12).  After the last stage of a
+// workgroup that decode works on stale registers and is never used.
+template <int n>
+__device__ __forceinline__ void fast_step(const FastStage& S, FastPipe& P, f32x16 (&acc)[4][4], const FastLane& L) {
+  constexpr int s = n >> 2, t = n & 3;
+  if constexpr (t == 0 && s < 3) fast_read_sub(S, P, (s + 1) & 1, L, s + 1);
+  if constexpr (t == 2 && s < 3) fast_convert_scales(P, (s + 1) & 1);
+  if constexpr (n == 14) fast_convert_scales(P, 0);
+  constexpr int c = n & 1, x = c ^ 1;
+  // the next step: word t1 of the sub-chunk in buffer u1
+  constexpr int t1 = (n + 1) & 3, u1 = n < 15 ? ((n + 1) >> 2) & 1 : 0;
+  constexpr bool hi = t1 >= 2;
+  {
+    const uint4* A = P.ca[u1];
+    const uint4* B = P.cb[u1];
+    // blocks 0-1 decode the next step's A frags, blocks 2-3 its B frags
+    mfma4_decode2<hi>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
+                      word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1]);
+    mfma4_decode2<hi>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
+                      word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3]);
+    mfma4_decode2<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
+                      word_of(B[1], t1), P.sb[u1][1], P.bv[x][0], P.bv[x][1]);
+    mfma4_decode2<hi>(acc[3][0], acc[3][1], acc[3][2], acc[3][3], P.bv[c][3], P.av[c], word_of(B[2], t1), P.sb[u1][2],
+                      word_of(B[3], t1), P.sb[u1][3], P.bv[x][2], P.bv[x][3]);
   }
+}
+
+// One stage (K = 256 = 4 sub-chunks x 4 k16-steps) from LDS stage S.  S is
+// last read at step 8, so before step 12 the waves synchronize (after which
+// every copy into Sn has landed and nobody reads S any more), `refill`
+// issues the copies of the stage after next into S, and sub-chunk 0 of Sn is
+// read for the decode carried by step 15 (after the last stage of a
+// workgroup Sn holds stale data, read but never used).
+template <typename Refill>
+__device__ __forceinline__ void fast_stage(const FastStage& S, const FastStage& Sn, FastPipe& P, f32x16 (&acc)[4][4],
+                                           const FastLane& L, Refill&& refill) {
+  fast_step<0>(S, P, acc, L);
+  fast_step<1>(S, P, acc, L);
+  fast_step<2>(S, P, acc, L);
+  fast_step<3>(S, P, acc, L);
+  fast_step<4>(S, P, acc, L);
+  fast_step<5>(S, P, acc, L);
+  fast_step<6>(S, P, acc, L);
+  fast_step<7>(S, P, acc, L);
+  fast_step<8>(S, P, acc, L);
+  fast_step<9>(S, P, acc, L);
+  fast_step<10>(S, P, acc, L);
+  fast_step<11>(S, P, acc, L);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  refill();
+  fast_read_sub(Sn, P, 0, L, 0);
+  fast_step<12>(S, P, acc, L);
+  fast_step<13>(S, P, acc, L);
+  fast_step<14>(S, P, acc, L);
+  fast_step<15>(S, P, acc, L);
 }
 
 // Epilogue of one tile: lane (r, h), accumulator element e of MFMA tile (j, i)
@@ -610,10 +650,11 @@ __device__ __forceinline__ void fast_epilogue(const f32x16 (&acc)[4][4], void* _
 // Persistent fast-path kernel: one workgroup per CU walks tiles lin, lin + G,
 // lin + 2G, ... (G = grid size).  Workgroups are dealt round-robin to the 8
 // XCDs, so lin is remapped to keep the tiles processed concurrently by one
-// XCD contiguous (they then share A and B rows in that XCD's L2).  The first
-// stage of the next tile is fetched during the last stage of the current one
-// and the epilogue stores are not waited for, so neither the store drain,
-// the workgroup turnover nor the first fetch stalls the matrix cores.
+// XCD contiguous (they then share A and B rows in that XCD's L2).  Stages
+// stream through the two LDS stages across tile boundaries: the copies of
+// the next tile's first two stages are issued during the current tile's last
+// two, and the epilogue stores are not waited for, so neither the store
+// drain, the tile turnover nor the first fetch stalls the matrix cores.
 template <bool kBf16Out>
 __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
@@ -625,7 +666,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int lin0 = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
-  const int nk = K / kFastKC;  // even
+  const int nk = K / kFastKC;  // even, >= 2
   const float g = a_sg[0] * b_sg[0];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -633,13 +674,27 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   const int r = lane & 31, h = lane >> 5;
 
   const FastLoad ld = fast_load_offsets(K);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)&st0);
+  const uint32_t lds1 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)&st1);
   int tm, tn;
   tile_of_lin(lin0, tiles_m, tiles_n, tm, tn);
   bool edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTile > N;
-  fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
+  fast_load_stage(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
                   K, 0);
+  fast_load_stage(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
+                  K, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  FastLane L;
+  L.a = (uint32_t)(wm * 128 + r) * 128;
+  L.b = (uint32_t)(wn * 128 + r) * 128;
+  L.sa = (uint32_t)(wm * 128 + r) * 16 + 2 * h;
+  L.sb = (uint32_t)(wn * 128 + r) * 16 + 2 * h;
+  L.hsw = 16u * (uint32_t)(h ^ ((r >> 1) & 7));
+  FastPipe P;
+  fast_read_sub(st0, P, 0, L, 0);
+  fast_convert_scales(P, 0);
+  fast_decode_first(P);
 
   for (int lin = lin0; lin < T; lin += G) {
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
@@ -647,30 +702,32 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     int tm_next = tm, tn_next = tn;
     if (has_next) tile_of_lin(lin + G, tiles_m, tiles_n, tm_next, tn_next);
     const bool edge_next = (int64_t)(tm_next + 1) * kTile > M || (int64_t)(tn_next + 1) * kTile > N;
+    const int64_t m0_next = (int64_t)tm_next * kTile, n0_next = (int64_t)tn_next * kTile;
     f32x16 acc[4][4];
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[j][i] = f32x16{};
     for (int kc = 0; kc < nk; kc += 2) {
-      fast_load_stage(st1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 1);
-      fast_compute_stage(st0, acc, wm, wn, r, h);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      // st0 is free: fetch the next stage of this tile, or during the last
-      // stage the first stage of the next tile, so that it is complete at the
-      // barrier below and the epilogue stores never have to be waited for.
-      if (kc + 2 < nk)
-        fast_load_stage(st0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
-      else if (has_next)
-        fast_load_stage(st0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, (int64_t)tm_next * kTile,
-                        (int64_t)tn_next * kTile, M, N, K, 0);
-      fast_compute_stage(st1, acc, wm, wn, r, h);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // stage kc (st0), then kc + 1 (st1); each refills its LDS stage with
+      // the stage two later: kc + 2 of this tile or, at the end of the tile,
+      // stage 0 / 1 of the next tile.
+      const bool more = kc + 2 < nk;
+      fast_stage(st0, st1, P, acc, L, [&] {
+        if (more)
+          fast_load_stage(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+        else if (has_next)
+          fast_load_stage(lds0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 0);
+      });
+      fast_stage(st1, st0, P, acc, L, [&] {
+        if (more)
+          fast_load_stage(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 3);
+        else if (has_next)
+          fast_load_stage(lds1, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 1);
+      });
     }
-    // The stores drain while the next tile computes (its first s_waitcnt comes
-    // a whole stage later).
+    // The stores drain while the next tile computes (the next wait comes
+    // 12 k16-steps later).
     fast_epilogue<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
     tm = tm_next;
     tn = tn_next;

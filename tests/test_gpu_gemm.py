@@ -124,3 +124,25 @@ def test_gemm_many_tiles_with_ragged_edges():
     check_gemm_bound(c[rows], ref, tot, True, "many tiles rows")
     ref, tot = oracle.gemm_ref(*ao, *bo, cols=cols)
     check_gemm_bound(c[:, cols], ref, tot, True, "many tiles cols")
+
+
+@pytest.mark.parametrize("K", [48, 512, 1024])
+def test_gemm_every_scale_byte(K):
+    """Every finite E4M3 scale byte (0x00..0x7E, subnormals included) on both
+    operands, random codes, s_g = 1: within the bound of the fp64 reference.
+    K = 48 runs the general kernel, K % 512 == 0 the direct-to-LDS one."""
+    nv = _nv()
+    rng = np.random.default_rng(K)
+    M, N = 260, 264
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    m_i, kb_i = np.meshgrid(np.arange(M), np.arange(K // 16), indexing="ij")
+    sa = ((m_i + 7 * kb_i) % 127).astype(np.uint8)
+    n_i, kb_j = np.meshgrid(np.arange(N), np.arange(K // 16), indexing="ij")
+    sb = ((3 * n_i + 5 * kb_j + 11) % 127).astype(np.uint8)
+    assert set(np.unique(sa)) == set(range(127)) and set(np.unique(sb)) == set(range(127))
+    one = torch.ones(1, device=dev())
+    t = lambda a: torch.from_numpy(a).to(dev())
+    c = nv.gemm((t(ac), t(sa), one), (t(bc), t(sb), one), out_dtype=torch.float32)
+    ref, tot = oracle.gemm_ref(ac, sa, 1.0, bc, sb, 1.0)
+    check_gemm_bound(c_to_f64(c), ref, tot, False, "every scale byte K=%d" % K)
