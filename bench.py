@@ -16,9 +16,20 @@ secondary HBM throughputs (activation quantize of the FFN down-projection
 input, NVFP4 KV-cache round trip), and the CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 10]
+
+Before the W warm-up steps the step runs for SETTLE_S seconds: the GPU's
+clocks take tens of milliseconds of sustained load to settle (the GEMM's
+kernel time drifts by up to 30% over its first ~30 launches), and the timed
+steps are meant to measure the steady state.
+
+roofline.traffic is the GEMM kernel's HBM bytes per launch from rocprofv3
+FETCH_SIZE / WRITE_SIZE counters (profiles/), scaled by what the same
+counters read for a 1 GiB device copy; it is reported only while the GEMM
+sources hash to the ones the counters were taken on, else null.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +38,14 @@ import time
 METRIC = "W4A4 NVFP4 GEMM TFLOP/s (M16384 K3072 N14336) + quant/dequant HBM GB/s"
 MFMA_PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+SETTLE_S = 0.5
+GEMM_KERNEL = "gemm_w4a4_fast_kernel"
+GEMM_SOURCES = ("long_video_dit_amd/csrc/nvfp4_gemm.hip", "long_video_dit_amd/csrc/nvfp4_device.h")
+# HBM byte counters of one GEMM launch (FFN up-projection, bf16 out), KiB per dispatch, and the
+# factors that map them to bytes (a 1 GiB copy reads FETCH_SIZE = 512 MiB, WRITE_SIZE = 1 GiB).
+# Taken with profiles/gemm_w4a4_fast_kernel_ffn_up_16384x14336x3072.md's commands.
+GEMM_COUNTERS = {"sources_sha256": "fc382456baf8b9b91fd2489a9beb1164e055bdc81d6d3cbfe89977a2b3602a50",
+                 "fetch_kib": 326565.9, "write_kib": 490737.2, "fetch_scale": 2.0, "write_scale": 1.0}
 # Whole-pass HBM bytes per element (bf16 data, 4-bit code + one 8-bit scale per 16 elements).
 B_AMAX = 2.0
 B_ENCODE = 2.0 + 0.5 + 1.0 / 16
@@ -40,12 +59,15 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--no-secondary", action="store_true", help="skip the quantize / KV-cache bandwidth lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--all-configs", action="store_true",
+                   help="instead of the step: time every workload (quantize, GEMM, KV cache) and the oracle "
+                        "on a bounded sample of each, one JSON line")
     return p.parse_args()
 
 
@@ -67,6 +89,23 @@ def time_calls(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def sources_sha256(root):
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic(root):
+    """HBM bytes per GEMM launch from the recorded counters, or None when the
+    kernel sources changed since they were taken."""
+    c = GEMM_COUNTERS
+    if c["sources_sha256"] is None or c["sources_sha256"] != sources_sha256(root):
+        return None
+    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -85,6 +124,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.all_configs:
+        print(json.dumps({"all_configs": all_configs(torch, nvfp4, workloads, dev, args.steps, args.warmup)}),
+              flush=True)
+        return
     cfg = workloads.CONFIGS[3]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     flop = 2.0 * M * N * K
@@ -110,6 +153,8 @@ def main():
         if i is not None:
             gemm_e[i].record()
 
+    log("settling clocks for %.1f s" % SETTLE_S)
+    settle(torch, step)
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
@@ -140,9 +185,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["workload"], "M": M, "N": N, "K": K, "a_dtype": "bf16", "c_dtype": "bf16",
                    "w_format": "nvfp4", "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_w4a4_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": GEMM_KERNEL, "achieved": round(achieved, 1),
                      "peak": MFMA_PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": gemm_traffic(root),
+                     "algorithmic_bytes": M * (K // 2 + K // 16) + N * (K // 2 + K // 16) + 2 * M * N + 8,
                      "gemm_ms": round(gemm_ms, 4)},
     }
     log("step %.3f ms, gemm %.3f ms -> %.1f TFLOP/s step, %.1f TFLOP/s gemm" % (ms_per_step, gemm_ms, value,
@@ -204,6 +250,99 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     res["hbm_peak_GB/s"] = HBM_PEAK_GBS
     log("secondary", json.dumps(res))
     return res
+
+
+def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
+    """Every workload at full size: GPU times from HIP events (warm, after the
+    clock-settling phase), and the CPU oracle timed on a bounded row sample
+    and scaled linearly to the full size (quantize includes the full amax)."""
+    import numpy as np
+    import oracle
+
+    res = {}
+    for cfg in (1, 2, 3, 4):
+        c = workloads.CONFIGS[cfg]
+        a_cpu, w_cpu = workloads.activations(cfg), workloads.weights(cfg)
+        a, w = a_cpu.to(dev), w_cpu.to(dev)
+        M, K = a.shape
+        N = w.shape[0]
+        wq = nvfp4.quantize(w)
+        aq = (torch.empty(M, K // 2, dtype=torch.uint8, device=dev),
+              torch.empty(M, K // 16, dtype=torch.uint8, device=dev),
+              torch.empty(1, dtype=torch.float32, device=dev))
+        out = torch.float32 if c["c_dtype"] == "f32" else torch.bfloat16
+        cbuf = torch.empty(M, N, dtype=out, device=dev)
+        quant = lambda: nvfp4.quantize(a, out=aq[:2], s_g_out=aq[2])
+        gemm = lambda: nvfp4.gemm(aq, wq, out=cbuf)
+        quant()
+        settle(torch, gemm)
+        q_ms = time_calls(torch, quant, steps, warmup)
+        g_ms = time_calls(torch, gemm, steps, warmup)
+        f_ms = time_calls(torch, lambda: nvfp4.gemm_fused_act(a, wq, out=cbuf, a_q=aq), steps, warmup)
+        esz = a.element_size()
+        qbytes = M * K * (2 * esz + 0.5625)
+        flop = 2.0 * M * N * K
+        # oracle on a bounded sample
+        to_np = (lambda t: t.numpy()) if a_cpu.dtype == torch.float32 else workloads.bf16_bits
+        an, wn = to_np(a_cpu), to_np(w_cpu)
+        wo = oracle.quantize(wn)
+        rows = min(M, max(1, int(2.0e9 / (2.0 * N * K))))  # about 2 s of fp64 dot products
+        t0 = time.perf_counter()
+        g = oracle.global_scale(oracle.amax(an))  # full tensor
+        ta = time.perf_counter()
+        ao = oracle.quantize(np.ascontiguousarray(an[:rows]), s_g=g)
+        t1 = time.perf_counter()
+        oracle.gemm_ref(*ao, *wo)
+        t2 = time.perf_counter()
+        oq_ms = (ta - t0) * 1e3 + (t1 - ta) * 1e3 * M / rows
+        og_ms = (t2 - t1) * 1e3 * M / rows
+        res[c["workload"]] = {
+            "M": M, "N": N, "K": K, "a_dtype": c["a_dtype"], "c_dtype": c["c_dtype"],
+            "quantize_ms": round(q_ms, 4), "quantize_GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(flop / (g_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp16_peak": round(flop / (g_ms * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
+            "fused_act_ms": round(f_ms, 4), "fused_act_TFLOP/s": round(flop / (f_ms * 1e-3) / 1e12, 1),
+            "oracle_quantize_ms_est": round(oq_ms, 1), "oracle_gemm_ms_est": round(og_ms, 1),
+            "oracle_sample_rows": rows, "oracle_threads": oracle.num_threads()}
+        log("config", cfg, json.dumps(res[c["workload"]]))
+        del a, w, wq, aq, cbuf
+        torch.cuda.empty_cache()
+    c = workloads.CONFIGS[5]
+    k_cpu, v_cpu = workloads.kv_cache()
+    k, v = k_cpu.to(dev), v_cpu.to(dev)
+    H, T, D = k.shape
+    qk, qv = nvfp4.kv_quantize(k), nvfp4.kv_quantize(v)
+    ok, ov = torch.empty_like(k), torch.empty_like(v)
+
+    def rt():
+        nvfp4.kv_quantize(k, out=qk)
+        nvfp4.kv_quantize(v, out=qv)
+        nvfp4.kv_dequantize(*qk, out=ok)
+        nvfp4.kv_dequantize(*qv, out=ov)
+
+    settle(torch, rt)
+    rt_ms = time_calls(torch, rt, steps, warmup)
+    n = 2 * k.numel()
+    kb = workloads.bf16_bits(k_cpu[:1])
+    t0 = time.perf_counter()
+    oc, os_, oh = oracle.kv_quantize(kb)
+    oracle.kv_dequantize(oc, os_, oh)
+    o_ms = (time.perf_counter() - t0) * 1e3 * 2 * H
+    res[c["workload"]] = {"H": H, "T": T, "D": D, "tensors": 2, "roundtrip_ms": round(rt_ms, 4),
+                          "roundtrip_GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (rt_ms * 1e-3) / 1e9, 1),
+                          "oracle_roundtrip_ms_est": round(o_ms, 1), "oracle_sample": "1 head of K",
+                          "oracle_threads": oracle.num_threads()}
+    log("config 5", json.dumps(res[c["workload"]]))
+    return res
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn back to back for `seconds` so that the clocks reach steady state."""
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(workloads, M, N, K, rows=8192):
