@@ -23,6 +23,7 @@
 // consecutive tiles land on the same XCD (ids are dealt round-robin over the
 // 8 XCDs), then grouped 8 tile-rows high for L2 reuse.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
@@ -620,28 +621,96 @@ __device__ __forceinline__ void fast_stage(const FastStage& S, const FastStage& 
 // Epilogue of one tile: lane (r, h), accumulator element e of MFMA tile (j, i)
 // is output row m = 32 i + r and column n = 32 j + 8 (e / 4) + 4 h + e % 4;
 // one 8-byte (bf16) or 16-byte (fp32) store per 4 consecutive columns.
+// The accumulators of one MFMA tile, read out only where the epilogue uses
+// them.  Without the empty asm the compiler reads all 256 accumulators into
+// VGPRs ahead of the full/edge branch (both paths read them), runs out of
+// VGPRs and spills; the reloads then wait, since vmcnt also counts stores,
+// for every output store issued before them.
+__device__ __forceinline__ f32x16 pinned(const f32x16& acc) {
+  f32x16 a = acc;
+  asm volatile("" : "+a"(a));
+  return a;
+}
+
 template <bool kBf16Out>
-__device__ __forceinline__ void fast_epilogue(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0, int64_t n0,
-                                              int M, int N, int wm, int wn, int r, int h, float g) {
+__device__ __forceinline__ void fast_store4(void* __restrict__ c, int64_t idx, const f32x16& a, int gq, float g) {
+  const float v0 = a[4 * gq] * g, v1 = a[4 * gq + 1] * g, v2 = a[4 * gq + 2] * g, v3 = a[4 * gq + 3] * g;
+  if constexpr (kBf16Out) {
+    const bf16x2 p0 = {(__bf16)v0, (__bf16)v1}, p1 = {(__bf16)v2, (__bf16)v3};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + idx) =
+        u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(c) + idx) = f32x4{v0, v1, v2, v3};
+  }
+}
+
+// Tiles that cross row M or column N: every store checks its row and column.
+template <bool kBf16Out>
+__device__ __forceinline__ void fast_epilogue_edge(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+                                                   int64_t n0, int M, int N, int wm, int wn, int r, int h, float g) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t m = m0 + wm * 128 + 32 * i + r;
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+      const f32x16 a = pinned(acc[j][i]);
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) {
         const int64_t n = n0 + wn * 128 + 32 * j + 8 * gq + 4 * h;
         if (n >= N) continue;  // N % 4 == 0: the 4 columns are all in or all out
-        const float v0 = acc[j][i][4 * gq] * g, v1 = acc[j][i][4 * gq + 1] * g;
-        const float v2 = acc[j][i][4 * gq + 2] * g, v3 = acc[j][i][4 * gq + 3] * g;
-        if constexpr (kBf16Out) {
-          const bf16x2 p0 = {(__bf16)v0, (__bf16)v1}, p1 = {(__bf16)v2, (__bf16)v3};
-          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(c) + m * N + n) =
-              u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(c) + m * N + n) = f32x4{v0, v1, v2, v3};
+        fast_store4<kBf16Out>(c, m * N + n, a, gq, g);
+      }
+    }
+  }
+}
+
+// Two packed bf16 of a[4 gq + 2 e], a[4 gq + 2 e + 1] times g.
+__device__ __forceinline__ uint32_t bf16_pair(const f32x16& a, int gq, int e, float g) {
+  const bf16x2 p = {(__bf16)(a[4 * gq + 2 * e] * g), (__bf16)(a[4 * gq + 2 * e + 1] * g)};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// Full tiles of an output with fewer than 2^32 elements: no checks, one row
+// pointer per MFMA row.  bf16: the lanes (r, 0) and (r, 1) hold adjacent
+// 4-column groups of one row; one swap of their halves (v_permlane32_swap)
+// gives each lane 8 consecutive columns, so every store writes 16 bytes per
+// lane and 32 bytes per row, halving the store instructions and the partial-
+// line write requests that the L2 has to merge.
+template <bool kBf16Out>
+__device__ __forceinline__ void fast_epilogue_full(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+                                                   int64_t n0, int N, int wm, int wn, int r, int h, float g) {
+  const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128 + r);
+  if constexpr (kBf16Out) {
+    const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 8 * h);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      __bf16* row = reinterpret_cast<__bf16*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const f32x16 a = pinned(acc[j][i]);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+          // columns 16 q + 0..3 (+4 on lanes h = 1) and 16 q + 8..11 (+4)
+          const auto s0 = __builtin_amdgcn_permlane32_swap(bf16_pair(a, 2 * q, 0, g), bf16_pair(a, 2 * q + 1, 0, g),
+                                                           false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(bf16_pair(a, 2 * q, 1, g), bf16_pair(a, 2 * q + 1, 1, g),
+                                                           false, false);
+          // lane h = 0 now holds columns 16 q + 0..7, lane h = 1 columns 16 q + 8..15
+          *reinterpret_cast<u32x4*>(row + 32 * j + 16 * q) = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
+      }
+    }
+  } else {
+    const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 4 * h);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float* row = reinterpret_cast<float*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const f32x16 a = pinned(acc[j][i]);
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) fast_store4<false>(row + 32 * j + 8 * gq, 0, a, gq, g);
       }
     }
   }
@@ -668,6 +737,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   const int lin0 = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
   const int nk = K / kFastKC;  // even, >= 2
   const float g = a_sg[0] * b_sg[0];
+  const bool small_c = (int64_t)M * N < (int64_t(1) << 32);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -692,11 +762,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   L.sb = (uint32_t)(wn * 128 + r) * 16 + 2 * h;
   L.hsw = 16u * (uint32_t)(h ^ ((r >> 1) & 7));
   FastPipe P;
-  fast_read_sub(st0, P, 0, L, 0);
-  fast_convert_scales(P, 0);
-  fast_decode_first(P);
 
   for (int lin = lin0; lin < T; lin += G) {
+    // First k16-step of the tile, from stage 0 in st0.  Decoding it here
+    // rather than in the previous tile's last step keeps the pipeline
+    // registers dead across the epilogue, which then has the VGPRs it needs
+    // (spill reloads there would wait for all of the tile's output stores).
+    fast_read_sub(st0, P, 0, L, 0);
+    fast_convert_scales(P, 0);
+    fast_decode_first(P);
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
     const bool has_next = lin + G < T;
     int tm_next = tm, tn_next = tn;
@@ -728,7 +802,10 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     }
     // The stores drain while the next tile computes (the next wait comes
     // 12 k16-steps later).
-    fast_epilogue<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
+    if (!edge && small_c)
+      fast_epilogue_full<kBf16Out>(acc, c, m0, n0, N, wm, wn, r, h, g);
+    else
+      fast_epilogue_edge<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
     tm = tm_next;
     tn = tn_next;
     edge = edge_next;
