@@ -329,8 +329,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w4a4_kernel(
 // decode or a scale conversion that the matrix cores would wait for.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// global -> LDS copy of 16 (or 4) bytes per lane: lane i reads base +
-// voff[i] and writes LDS address lds + 16 i (or 4 i); lds and base are
+// global -> LDS copy of 16 bytes per lane: lane i reads base + voff[i] and
+// writes LDS address lds + 16 i; lds and base are
 // wave-uniform (M0 and an SGPR pair).  Issued as asm statements without
 // outputs so that the compiler does not track these LDS writes (its tracking
 // falls back to waiting for every outstanding copy before any LDS read, which
@@ -343,9 +343,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
-}
-__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -362,15 +359,15 @@ constexpr uint32_t kStA = 0, kStB = kTile * 128, kStSA = 2 * kTile * 128, kStSB 
 
 // Copies of one stage (K = 256 of a 256-row tile of A and of B) issued by one
 // thread: wave w fills rows 64 w .. 64 w + 63 of both operands, 8 rows (1 KiB
-// of codes) per 16-byte copy instruction and 16 rows of scale bytes per
-// 4-byte copy.  For a full tile the per-lane part of each source offset only
+// of codes) per 16-byte copy instruction and all 64 rows of scale bytes (16
+// per row and stage, 16-byte aligned since K % 512 == 0) with one more.  For a full tile the per-lane part of each source offset only
 // depends on the lane and on the instruction's parity (the plane swizzle
 // q ^ ((row / 2) % 8) repeats every 16 rows), so it is kept in 3 VGPRs and
 // the row advance goes into the uniform SGPR base.  Tiles that cross the
 // last row of A or B clamp every lane's row and take the per-lane path.
 struct FastLoad {
   uint32_t vo[2];  // code offsets of even / odd instructions (full tiles)
-  uint32_t vs;     // scale offset (full tiles)
+  uint32_t vs;     // scale row offset (full tiles)
 };
 
 __device__ __forceinline__ FastLoad fast_load_offsets(int K) {
@@ -383,7 +380,7 @@ __device__ __forceinline__ FastLoad fast_load_offsets(int K) {
     const uint32_t q = (lane & 7) ^ ((row >> 1) & 7);
     o.vo[p] = (uint32_t)(lane >> 3) * row_bytes + 16 * q;
   }
-  o.vs = (uint32_t)(lane >> 2) * srow_bytes + 4 * (lane & 3);
+  o.vs = (uint32_t)lane * srow_bytes;
   return o;
 }
 
@@ -406,14 +403,9 @@ __device__ __forceinline__ void fast_load_stage(uint32_t lds, const FastLoad& o,
       lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], lds + kStA + slot0 * 16);
       lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], lds + kStB + slot0 * 16);
     }
-    const uint8_t* as = a_scales + (m0 + 64 * w) * srow_bytes + kc * 16;
-    const uint8_t* bs = b_scales + (n0 + 64 * w) * srow_bytes + kc * 16;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint32_t d0 = (uint32_t)(w * 4 + i) * 64;
-      lds_dma4(as + 16 * i * srow_bytes, o.vs, lds + kStSA + d0 * 4);
-      lds_dma4(bs + 16 * i * srow_bytes, o.vs, lds + kStSB + d0 * 4);
-    }
+    const uint32_t d0 = (uint32_t)w * 64 * 16;
+    lds_dma16(a_scales + (m0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + kStSA + d0);
+    lds_dma16(b_scales + (n0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + kStSB + d0);
     return;
   }
   const uint8_t* ac = a_codes + kc * 128;
@@ -428,17 +420,12 @@ __device__ __forceinline__ void fast_load_stage(uint32_t lds, const FastLoad& o,
     lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, lds + kStA + (uint32_t)slot0 * 16);
     lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, lds + kStB + (uint32_t)slot0 * 16);
   }
-  const uint8_t* as = a_scales + kc * 16;
-  const uint8_t* bs = b_scales + kc * 16;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int d0 = (w * 4 + i) * 64;
-    const int row = (d0 + lane) >> 2;
-    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
-    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-    lds_dma4(as, (uint32_t)(ra * srow_bytes) + 4 * (lane & 3), lds + kStSA + (uint32_t)d0 * 4);
-    lds_dma4(bs, (uint32_t)(rb * srow_bytes) + 4 * (lane & 3), lds + kStSB + (uint32_t)d0 * 4);
-  }
+  const int row = 64 * w + lane;
+  const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+  const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+  const uint32_t d0 = (uint32_t)w * 64 * 16;
+  lds_dma16(a_scales + kc * 16, (uint32_t)(ra * srow_bytes), lds + kStSA + d0);
+  lds_dma16(b_scales + kc * 16, (uint32_t)(rb * srow_bytes), lds + kStSB + d0);
 }
 
 // Registers that carry the pipeline from step to step: the packed codes and
@@ -671,47 +658,58 @@ __device__ __forceinline__ uint32_t bf16_pair(const f32x16& a, int gq, int e, fl
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Full tiles of an output with fewer than 2^32 elements: no checks, one row
-// pointer per MFMA row.  bf16: the lanes (r, 0) and (r, 1) hold adjacent
-// 4-column groups of one row; one swap of their halves (v_permlane32_swap)
-// gives each lane 8 consecutive columns, so every store writes 16 bytes per
-// lane and 32 bytes per row, halving the store instructions and the partial-
-// line write requests that the L2 has to merge.
-template <bool kBf16Out>
-__device__ __forceinline__ void fast_epilogue_full(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
-                                                   int64_t n0, int N, int wm, int wn, int r, int h, float g) {
-  const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128 + r);
-  if constexpr (kBf16Out) {
-    const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 8 * h);
+// Full tiles of an output with fewer than 2^32 elements, bf16: the output is
+// staged through a wave-private 4 KiB LDS chunk (32 rows x 64 columns, the
+// 16-byte pieces of row r at slot ^ (r / 2) % 8, conflict-free both ways) so
+// that every global store writes whole 128-byte lines of 8 rows; the L2
+// then merges no partial lines.  Lane (r, h) writes its 8-byte groups in the
+// MFMA layout; lane L reads back 16 bytes, row L / 8 + 8 k, slot L % 8.
+__device__ __forceinline__ void fast_epilogue_full_bf16(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+                                                        int64_t n0, int N, int wm, int wn, int r, int h, float g,
+                                                        uint8_t* wl) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wsw = (uint32_t)((r >> 1) & 7);
+  uint8_t* const wrow = wl + r * 128 + 8 * h;
+  const int rr0 = lane >> 3, slot = lane & 7;
+  const uint32_t out0 = (uint32_t)m0 + (uint32_t)(wm * 128);
+  const uint32_t lane_off = (uint32_t)rr0 * (uint32_t)N + (uint32_t)(n0 + wn * 128 + 8 * slot);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      __bf16* row = reinterpret_cast<__bf16*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
+  for (int i = 0; i < 4; i++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const f32x16 a = pinned(acc[j][i]);
+    for (int jp = 0; jp < 2; jp++) {
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-          // columns 16 q + 0..3 (+4 on lanes h = 1) and 16 q + 8..11 (+4)
-          const auto s0 = __builtin_amdgcn_permlane32_swap(bf16_pair(a, 2 * q, 0, g), bf16_pair(a, 2 * q + 1, 0, g),
-                                                           false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(bf16_pair(a, 2 * q, 1, g), bf16_pair(a, 2 * q + 1, 1, g),
-                                                           false, false);
-          // lane h = 0 now holds columns 16 q + 0..7, lane h = 1 columns 16 q + 8..15
-          *reinterpret_cast<u32x4*>(row + 32 * j + 16 * q) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      for (int jj = 0; jj < 2; jj++) {
+        const f32x16 a = pinned(acc[2 * jp + jj][i]);
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+          const uint32_t chunk = (uint32_t)(4 * jj + gq);
+          *reinterpret_cast<u32x2*>(wrow + 16 * (chunk ^ wsw)) = u32x2{bf16_pair(a, gq, 0, g), bf16_pair(a, gq, 1, g)};
         }
       }
-    }
-  } else {
-    const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 4 * h);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float* row = reinterpret_cast<float*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const f32x16 a = pinned(acc[j][i]);
-#pragma unroll
-        for (int gq = 0; gq < 4; gq++) fast_store4<false>(row + 32 * j + 8 * gq, 0, a, gq, g);
+      for (int k = 0; k < 4; k++) {
+        const int rr = rr0 + 8 * k;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(wl + rr * 128 + 16 * (slot ^ ((rr >> 1) & 7)));
+        __bf16* dst = reinterpret_cast<__bf16*>(c) + ((out0 + 32u * i + 8u * k) * (uint32_t)N + lane_off + 64u * jp);
+        *reinterpret_cast<u32x4*>(dst) = v;
       }
+    }
+  }
+}
+
+// Full tiles, fp32 output: 16-byte stores straight from the MFMA layout.
+__device__ __forceinline__ void fast_epilogue_full_f32(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+                                                       int64_t n0, int N, int wm, int wn, int r, int h, float g) {
+  const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128 + r);
+  const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 4 * h);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float* row = reinterpret_cast<float*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f32x16 a = pinned(acc[j][i]);
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) fast_store4<false>(row + 32 * j + 8 * gq, 0, a, gq, g);
     }
   }
 }
@@ -731,6 +729,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
   __shared__ FastStage st0;
   __shared__ FastStage st1;
+  __shared__ __attribute__((aligned(16))) uint8_t epi[4][4096];  // per-wave output staging (bf16)
   const int T = tiles_m * tiles_n;
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -802,9 +801,12 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     }
     // The stores drain while the next tile computes (the next wait comes
     // 12 k16-steps later).
-    if (!edge && small_c)
-      fast_epilogue_full<kBf16Out>(acc, c, m0, n0, N, wm, wn, r, h, g);
-    else
+    if (!edge && small_c) {
+      if constexpr (kBf16Out)
+        fast_epilogue_full_bf16(acc, c, m0, n0, N, wm, wn, r, h, g, epi[wave]);
+      else
+        fast_epilogue_full_f32(acc, c, m0, n0, N, wm, wn, r, h, g);
+    } else
       fast_epilogue_edge<kBf16Out>(acc, c, m0, n0, M, N, wm, wn, r, h, g);
     tm = tm_next;
     tn = tn_next;
@@ -825,8 +827,8 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   const bool bf = c_dtype == kDtypeBf16;
   const bool dma = (K % (2 * kFastKC) == 0) && (N % 4 == 0) && (M * (K / 2) < (int64_t(1) << 32)) &&
                    (N * (K / 2) < (int64_t(1) << 32)) && ((uintptr_t)a_codes % 16 == 0) &&
-                   ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 4 == 0) &&
-                   ((uintptr_t)b_scales % 4 == 0) && ((uintptr_t)c % 16 == 0);
+                   ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 16 == 0) &&
+                   ((uintptr_t)b_scales % 16 == 0) && ((uintptr_t)c % 16 == 0);
   if (dma) {
     const int T = tiles_m * tiles_n;
     const int cus = device_cu_count();
