@@ -338,11 +338,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt vmcnt(0) + s_barrier before a stage is read.  M0 is reserved by
 // the compiler, hence the warning pragma: the fast kernel contains no
 // compiler-generated use of M0 (tests/test_build_checks.py verifies this on
-// the generated assembly), so setting it here disturbs nothing.
+// the generated assembly), so setting it here disturbs nothing.  The s_nop
+// is the one wait state an LDS DMA needs after an SALU write of M0 (the
+// compiler's hazard recognizer does not look inside asm statements).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "m0");
 }
 #pragma clang diagnostic pop
 
