@@ -76,6 +76,23 @@ int nvfp4_abi_version(void);
 const char *nvfp4_status_string(int status);
 
 /*
+ * Per-tensor scale alone: s_g[0] = RN_f32(max |x| / (6 * 448)) for x
+ * [rows][k] (dtype F32 or BF16, row-major), the value nvfp4_quantize
+ * computes with NVFP4_SCALE_COMPUTE.  Pass it back with NVFP4_SCALE_GIVEN
+ * to quantize several tensors, or chunks of one tensor written at different
+ * times, against one scale.  The scale stays on the device (the yourai.pro
+ * page lists reduced KV-cache synchronization among the NVFP4 inference-path
+ * optimizations: no host round trip).  s_g is also the reduction slot: the
+ * call zeroes it, every workgroup folds in its maximum with one atomic max
+ * on the magnitude bits (order-free, so deterministic), and a last kernel
+ * rounds it in place; s_g must not be read or written by other work until
+ * the call has finished on `stream`.  rows == 0 gives s_g = 0.  Requires
+ * k > 0, k % 16 == 0, rows * k < 2^40.
+ */
+nvfp4_status_t nvfp4_global_scale(const void *x, int dtype, int64_t rows, int64_t k, float *s_g,
+                                  void *stream);
+
+/*
  * Quantize x [rows][k] (dtype F32 or BF16, row-major) to NVFP4.
  *   codes   [rows][k/2]  u8 out      scales [rows][k/16] u8 out
  *   s_g     [1] fp32: out with NVFP4_SCALE_COMPUTE, in with NVFP4_SCALE_GIVEN

@@ -63,6 +63,15 @@ const char* nvfp4_status_string(int status) {
   }
 }
 
+nvfp4_status_t nvfp4_global_scale(const void* x, int dtype, int64_t rows, int64_t k, float* s_g, void* stream) {
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  nvfp4_status_t st = check_matrix(rows, k, true);
+  if (st != NVFP4_OK) return st;
+  if (!s_g || (rows > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(s_g, 4) || !aligned(x, 16)) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_global_scale_slot(x, dtype, rows * k / 8, s_g, (hipStream_t)stream));
+}
+
 nvfp4_status_t nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
                               float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;

@@ -35,6 +35,9 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shm
 // units_per_group 8-element units, each run with its own s_g.
 hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group, int groups, uint32_t* partials,
                                int64_t partial_capacity, float* s_g, hipStream_t stream);
+// Standalone per-tensor scale: zero the s_g slot, atomic-max the magnitude
+// bits into it, round in place (three kernels, no scratch).
+hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream);
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
                          uint32_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,

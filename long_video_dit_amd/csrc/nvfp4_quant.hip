@@ -9,6 +9,7 @@
 //
 //   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
+//   amax_slot_kernel     standalone s_g: atomic max into the s_g slot itself
 //   encode_kernel        pass 2: scale byte per 16, 8 codes per lane
 //   dequant_kernel       codes + scales -> bf16 / fp32, 8 outputs per lane
 //
@@ -117,6 +118,36 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t* __re
   }
 }
 
+// ---- standalone per-tensor scale: the s_g slot is the reduction target ----
+
+// slot <- 0 (a kernel rather than a memset node, so the call can be captured).
+__global__ void zero_slot_kernel(uint32_t* __restrict__ slot) { slot[0] = 0u; }
+
+// Every workgroup folds the max |x| bits of its units into the slot with one
+// atomic max (order-free, so the result does not depend on scheduling).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_slot_kernel(const T* __restrict__ x, int64_t units,
+                                                             uint32_t* __restrict__ slot) {
+  __shared__ uint32_t smem[kThreads / 64];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; u + 3 * stride < units; u += 4 * stride) {
+    const uint32_t a = amax8_bits(x, u), b = amax8_bits(x, u + stride);
+    const uint32_t c = amax8_bits(x, u + 2 * stride), d = amax8_bits(x, u + 3 * stride);
+    m = __builtin_elementwise_max(m, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                                               __builtin_elementwise_max(c, d)));
+  }
+  for (; u < units; u += stride) m = __builtin_elementwise_max(m, amax8_bits(x, u));
+  m = block_max_u32(m, smem);
+  if (threadIdx.x == 0) atomicMax(slot, m);
+}
+
+// slot (max |x| as fp32 bits) -> s_g = RN(amax / 2688), in place.
+__global__ void finalize_slot_kernel(float* __restrict__ s_g) {
+  s_g[0] = __fdiv_rn(__uint_as_float(reinterpret_cast<const uint32_t*>(s_g)[0]), 2688.0f);
+}
+
 // grid: (X, G).  Each lane encodes 8-element units; the partner lane (lane ^ 1)
 // holds the other half of the 16-element block.
 template <typename T>
@@ -215,7 +246,7 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group
                                int64_t partial_capacity, float* s_g, hipStream_t stream) {
   const int cus = device_cu_count();
   // Partials per group: enough blocks to saturate HBM, bounded by the scratch.
-  int64_t P = grid_blocks(units_per_group, 8, (int)std::max<int64_t>(1, (int64_t)cus * 8 / groups));
+  int64_t P = grid_blocks(units_per_group, 8, (int)std::max<int64_t>(1, (int64_t)cus * 16 / groups));
   if (P * groups > partial_capacity) P = std::max<int64_t>(1, partial_capacity / groups);
   if (units_per_group == 0) {
     P = 0;
@@ -232,6 +263,21 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group
   }
   return launch_kernel(finalize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, (const uint32_t*)partials,
                        (int)P, s_g);
+}
+
+hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream) {
+  uint32_t* slot = reinterpret_cast<uint32_t*>(s_g);
+  hipError_t e = launch_kernel(zero_slot_kernel, dim3(1), dim3(1), 0, stream, slot);
+  if (e != hipSuccess) return e;
+  if (units > 0) {
+    const dim3 grid((unsigned)grid_blocks(units, 8, device_cu_count() * 16));
+    if (dtype == kDtypeF32)
+      e = launch_kernel(amax_slot_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units, slot);
+    else
+      e = launch_kernel(amax_slot_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, units, slot);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel(finalize_slot_kernel, dim3(1), dim3(1), 0, stream, s_g);
 }
 
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,

@@ -21,6 +21,7 @@ _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "nvfp4_abi_version": (_I, []),
     "nvfp4_status_string": (ctypes.c_char_p, [_I]),
+    "nvfp4_global_scale": (_I, [_P, _I, _I64, _I64, _P, _P]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
@@ -100,6 +101,15 @@ def quantize(x, s_g=None, out=None, s_g_out=None):
     _call("nvfp4_quantize", _ptr(x), _dt(x), rows, k, _ptr(codes), _ptr(scales), _ptr(s_g), flags,
           _stream(x.device))
     return codes, scales, s_g
+
+
+def global_scale(x, out=None):
+    """Per-tensor scale of x [rows, k] alone: f32 [1] = RN(max|x| / 2688), on the device."""
+    _need_cuda(x)
+    rows, k = x.shape
+    s_g = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    _call("nvfp4_global_scale", _ptr(x), _dt(x), rows, k, _ptr(s_g), _stream(x.device))
+    return s_g
 
 
 def dequantize(codes, scales, s_g, dtype=torch.bfloat16, out=None):

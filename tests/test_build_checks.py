@@ -67,6 +67,13 @@ def test_validation_errors_launch_nothing():
     assert lib.nvfp4_quantize(buf, 1, 4, 32, buf, buf, None, 0, None) == nv.ERR_NULL
     assert lib.nvfp4_quantize(odd, 1, 4, 32, buf, buf, buf, 0, None) == nv.ERR_ALIGN
     # dequantize
+    assert lib.nvfp4_global_scale(buf, 2, 4, 32, buf, None) == nv.ERR_DTYPE
+    assert lib.nvfp4_global_scale(buf, 1, 4, 40, buf, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_global_scale(buf, 1, -2, 32, buf, None) == nv.ERR_SHAPE
+    assert lib.nvfp4_global_scale(None, 1, 4, 32, buf, None) == nv.ERR_NULL
+    assert lib.nvfp4_global_scale(buf, 1, 4, 32, None, None) == nv.ERR_NULL
+    assert lib.nvfp4_global_scale(odd, 0, 4, 32, buf, None) == nv.ERR_ALIGN
+
     assert lib.nvfp4_dequantize(buf, buf, buf, 4, 32, buf, 3, None) == nv.ERR_DTYPE
     assert lib.nvfp4_dequantize(buf, buf, buf, 4, 40, buf, 1, None) == nv.ERR_SHAPE
     assert lib.nvfp4_dequantize(None, buf, buf, 4, 32, buf, 1, None) == nv.ERR_NULL

@@ -143,3 +143,52 @@ def test_quantize_deterministic():
     r2 = nv.quantize(a)
     for u, v in zip(r1, r2):
         assert torch.equal(u, v)
+
+
+def _global_scale_cases():
+    gen = torch.Generator().manual_seed(77)
+    yield "f32 3x48", torch.randn(3, 48, generator=gen)
+    yield "bf16 1x16", torch.randn(1, 16, generator=gen).to(torch.bfloat16)
+    yield "bf16 negative max", (torch.randn(257, 272, generator=gen).abs() * -3.0).to(torch.bfloat16)
+    yield "f32 tiny (s_g underflows to subnormal / zero)", torch.full((5, 32), 1e-41)
+    yield "f32 zeros", torch.zeros(64, 64)
+    yield "bf16 cfg2 activations (outliers)", workloads.activations(2)
+    yield "bf16 cfg4 activations", workloads.activations(4)
+
+
+@pytest.mark.parametrize("case", range(7))
+def test_global_scale_matches_oracle_and_quantize(case):
+    """nvfp4_global_scale = RN(amax / 2688), bit-exact to the oracle and to
+    the s_g that nvfp4_quantize computes; quantizing with it as a given scale
+    reproduces the computed-scale result."""
+    nv = _nv()
+    label, x_cpu = list(_global_scale_cases())[case]
+    log("global_scale", label, tuple(x_cpu.shape), x_cpu.dtype)
+    x = x_cpu.to(dev())
+    g = nv.global_scale(x)
+    q = nv.quantize(x)
+    qg = nv.quantize(x, s_g=g)
+    torch.cuda.synchronize()
+    xo = oracle_input(x_cpu)
+    want = np.float32(oracle.global_scale(oracle.amax(xo)))
+    got = g.cpu().numpy()[0]
+    assert got.view(np.uint32) == want.view(np.uint32), "%s: %r != %r" % (label, got, want)
+    assert torch.equal(g, q[2])
+    for u, v in zip(q[:2], qg[:2]):
+        assert torch.equal(u, v)
+
+
+def test_global_scale_empty_and_reuse():
+    """rows == 0 gives s_g = 0; the slot is fully overwritten on every call."""
+    nv = _nv()
+    s = torch.full((1,), 123.0, device=dev())
+    nv.global_scale(torch.empty(0, 32, dtype=torch.bfloat16, device=dev()), out=s)
+    torch.cuda.synchronize()
+    assert s.item() == 0.0
+    x = torch.randn(100, 64, device=dev())
+    nv.global_scale(x, out=s)
+    a = s.clone()
+    nv.global_scale(x * 0.5, out=s)
+    nv.global_scale(x, out=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, s)
