@@ -44,8 +44,8 @@ GEMM_SOURCES = ("long_video_dit_amd/csrc/nvfp4_gemm.hip", "long_video_dit_amd/cs
 # HBM byte counters of one GEMM launch (FFN up-projection, bf16 out), KiB per dispatch, and the
 # factors that map them to bytes (a 1 GiB copy reads FETCH_SIZE = 512 MiB, WRITE_SIZE = 1 GiB).
 # Taken with profiles/gemm_w4a4_fast_kernel_ffn_up_16384x14336x3072.md's commands.
-GEMM_COUNTERS = {"sources_sha256": "fc382456baf8b9b91fd2489a9beb1164e055bdc81d6d3cbfe89977a2b3602a50",
-                 "fetch_kib": 326565.9, "write_kib": 490737.2, "fetch_scale": 2.0, "write_scale": 1.0}
+GEMM_COUNTERS = {"sources_sha256": "4bfc004a09aef69b081d2c94230a5a0c8350863c54e2c9a85c09d309ed49077c",
+                 "fetch_kib": 300017.0, "write_kib": 458752.0, "fetch_scale": 2.0, "write_scale": 1.0}
 # Whole-pass HBM bytes per element (bf16 data, 4-bit code + one 8-bit scale per 16 elements).
 B_AMAX = 2.0
 B_ENCODE = 2.0 + 0.5 + 1.0 / 16
