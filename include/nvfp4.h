@@ -157,6 +157,24 @@ nvfp4_status_t kv_quantize(const void *kv, int64_t heads, int64_t tokens, int64_
                            uint8_t *codes, uint8_t *scales, float *head_scales, void *stream);
 
 /*
+ * Append to an NVFP4 KV cache in place: kv_new [heads][tokens_new][head_dim]
+ * bf16 is quantized with the per-head scales already in head_scales [heads]
+ * (frozen, e.g. from kv_quantize of the first chunk or from
+ * nvfp4_global_scale) and written to rows token_offset .. token_offset +
+ * tokens_new - 1 of each head of the cache codes [heads][cache_tokens]
+ * [head_dim/2] and scales [heads][cache_tokens][head_dim/16]; every other
+ * byte of the cache is left as it is.  Values beyond 2688 * head_scales[h]
+ * saturate (code 6 under scale 448).  Per the yourai.pro page (in-place
+ * updates of the quantized cache among the NVFP4 inference-path
+ * optimizations) and the arXiv abstract (NVFP4 KV cache).  Requires
+ * head_dim % 16 == 0, 0 <= token_offset, token_offset + tokens_new <=
+ * cache_tokens; tokens_new == 0 is a no-op.
+ */
+nvfp4_status_t kv_quantize_append(const void *kv_new, int64_t heads, int64_t tokens_new, int64_t head_dim,
+                                  const float *head_scales, uint8_t *codes, uint8_t *scales,
+                                  int64_t cache_tokens, int64_t token_offset, void *stream);
+
+/*
  * NVFP4 KV cache dequantize to bf16 [heads][tokens][head_dim]:
  *   out = RN_bf16(val(code) * val(scale) * head_scales[h]).
  * The "parallel dequantization" of the d9249.github.io review (section

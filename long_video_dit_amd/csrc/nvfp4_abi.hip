@@ -165,6 +165,23 @@ nvfp4_status_t kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_
                                        reinterpret_cast<uint32_t*>(codes), scales, s));
 }
 
+nvfp4_status_t kv_quantize_append(const void* kv_new, int64_t heads, int64_t tokens_new, int64_t head_dim,
+                                  const float* head_scales, uint8_t* codes, uint8_t* scales, int64_t cache_tokens,
+                                  int64_t token_offset, void* stream) {
+  nvfp4_status_t st = check_kv(heads, tokens_new, head_dim);
+  if (st == NVFP4_OK) st = check_kv(heads, cache_tokens, head_dim);
+  if (st != NVFP4_OK) return st;
+  if (token_offset < 0 || token_offset > cache_tokens || tokens_new > cache_tokens - token_offset) return NVFP4_ERR_SHAPE;
+  if (!head_scales || (tokens_new > 0 && (!kv_new || !codes || !scales))) return NVFP4_ERR_NULL;
+  if (!aligned(head_scales, 4) || !aligned(kv_new, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return NVFP4_ERR_ALIGN;
+  if (tokens_new == 0) return NVFP4_OK;
+  const int64_t units_new = tokens_new * head_dim / 8;  // 8-element units of one head's new rows
+  return from_hip(nvfp4::launch_encode(kv_new, nvfp4::kDtypeBf16, units_new, (int)heads, head_scales,
+                                       reinterpret_cast<uint32_t*>(codes), scales, (hipStream_t)stream,
+                                       cache_tokens * head_dim / 8, token_offset * head_dim / 8));
+}
+
 nvfp4_status_t kv_dequantize(const uint8_t* codes, const uint8_t* scales, const float* head_scales, int64_t heads,
                              int64_t tokens, int64_t head_dim, void* kv_out, void* stream) {
   nvfp4_status_t st = check_kv(heads, tokens, head_dim);

@@ -38,8 +38,11 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group
 // Standalone per-tensor scale: zero the s_g slot, atomic-max the magnitude
 // bits into it, round in place (three kernels, no scratch).
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream);
+// Encode pass; group g is written at unit g * out_group_stride + out_offset
+// (out_group_stride < 0: = units_per_group, a dense tensor).
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
-                         uint32_t* codes, uint8_t* scales, hipStream_t stream);
+                         uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride = -1,
+                         int64_t out_offset = 0);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
                           int groups, void* y, int y_dtype, hipStream_t stream);
 

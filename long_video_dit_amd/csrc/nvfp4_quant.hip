@@ -149,16 +149,21 @@ __global__ void finalize_slot_kernel(float* __restrict__ s_g) {
 }
 
 // grid: (X, G).  Each lane encodes 8-element units; the partner lane (lane ^ 1)
-// holds the other half of the 16-element block.
+// holds the other half of the 16-element block.  Group g reads units
+// [g * units_per_group, (g + 1) * units_per_group) of x and writes them at
+// unit g * out_group_stride + out_offset of the codes (and the matching scale
+// bytes): a plain tensor has out_group_stride = units_per_group and
+// out_offset = 0; a KV-cache append writes a slice of each head's rows.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, int64_t units_per_group,
                                                           const float* __restrict__ s_g,
                                                           uint32_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales) {
+                                                          uint8_t* __restrict__ scales, int64_t out_group_stride,
+                                                          int64_t out_offset) {
   const int g = blockIdx.y;
   const EncodeConsts c = make_encode_consts(s_g[g]);
-  const int64_t base = (int64_t)g * units_per_group;
-  const T* xg = x + base * 8;
+  const int64_t base = (int64_t)g * out_group_stride + out_offset;
+  const T* xg = x + (int64_t)g * units_per_group * 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   constexpr int U = 2;
   for (int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; u0 < units_per_group; u0 += U * stride) {
@@ -281,16 +286,18 @@ hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, flo
 }
 
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
-                         uint32_t* codes, uint8_t* scales, hipStream_t stream) {
+                         uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride,
+                         int64_t out_offset) {
   if (units_per_group == 0) return hipSuccess;
+  if (out_group_stride < 0) out_group_stride = units_per_group;
   const int cus = device_cu_count();
   const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 16 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (dtype == kDtypeF32)
     return launch_kernel(encode_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group, s_g,
-                         codes, scales);
+                         codes, scales, out_group_stride, out_offset);
   return launch_kernel(encode_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, units_per_group,
-                       s_g, codes, scales);
+                       s_g, codes, scales, out_group_stride, out_offset);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,

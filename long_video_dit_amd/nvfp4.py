@@ -28,6 +28,7 @@ SIGNATURES = {
     "nvfp4_gemm_fused_act": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _P]),
     "kv_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "kv_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P]),
 }
 
 _lib = None
@@ -162,6 +163,18 @@ def kv_quantize(kv, out=None):
         raise TypeError("kv_quantize expects bfloat16")
     _call("kv_quantize", _ptr(kv), H, T, D, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _stream(kv.device))
     return out
+
+
+def kv_quantize_append(kv_new, cache, token_offset):
+    """Quantize kv_new bf16 [H, t, D] with the cache's frozen per-head scales into rows
+    token_offset .. token_offset + t - 1 of cache = (codes [H, T, D/2], scales [H, T, D/16],
+    head_scales f32 [H]), in place.  Returns cache."""
+    _need_cuda(kv_new, *cache)
+    H, t, D = kv_new.shape
+    codes, scales, head_scales = cache
+    _call("kv_quantize_append", _ptr(kv_new), H, t, D, _ptr(head_scales), _ptr(codes), _ptr(scales),
+          codes.shape[1], token_offset, _stream(kv_new.device))
+    return cache
 
 
 def kv_dequantize(codes, scales, head_scales, out=None):

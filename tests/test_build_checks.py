@@ -93,6 +93,13 @@ def test_validation_errors_launch_nothing():
     assert lib.kv_quantize(buf, 0, 16, 128, buf, buf, buf, None) == nv.ERR_SHAPE
     assert lib.kv_quantize(buf, 4, 16, 120, buf, buf, buf, None) == nv.ERR_SHAPE
     assert lib.kv_quantize(buf, 4, 16, 128, buf, buf, None, None) == nv.ERR_NULL
+    assert lib.kv_quantize_append(buf, 4, 16, 128, buf, buf, buf, 64, 49, None) == nv.ERR_SHAPE  # past the cache
+    assert lib.kv_quantize_append(buf, 4, 16, 128, buf, buf, buf, 64, -1, None) == nv.ERR_SHAPE
+    assert lib.kv_quantize_append(buf, 4, 16, 120, buf, buf, buf, 64, 0, None) == nv.ERR_SHAPE
+    assert lib.kv_quantize_append(buf, 4, 16, 128, None, buf, buf, 64, 0, None) == nv.ERR_NULL
+    assert lib.kv_quantize_append(None, 4, 16, 128, buf, buf, buf, 64, 0, None) == nv.ERR_NULL
+    assert lib.kv_quantize_append(buf, 4, 16, 128, buf, odd, buf, 64, 0, None) == nv.ERR_ALIGN
+    assert lib.kv_quantize_append(buf, 4, 0, 128, buf, buf, buf, 64, 64, None) == nv.OK  # empty append
     assert lib.kv_dequantize(buf, buf, buf, 4, -1, 128, buf, None) == nv.ERR_SHAPE
     assert lib.kv_dequantize(buf, buf, buf, 4, 16, 128, odd, None) == nv.ERR_ALIGN
 

@@ -54,3 +54,34 @@ def test_kv_full_size():
     log("kv full", tuple(k.shape))
     _check(k, "K full")
     _check(v, "V full")
+
+
+@pytest.mark.parametrize("H,T,D,offset,t_new", [(4, 256, 128, 100, 48), (3, 64, 64, 63, 1), (24, 512, 128, 448, 64)])
+def test_kv_append_in_place(H, T, D, offset, t_new):
+    """A cache filled by kv_quantize, then new tokens appended at an offset with
+    the frozen head scales (some of them beyond the scale's range, which
+    saturate): the appended rows equal the oracle's quantization of the new
+    tokens under those scales, every other byte of the cache is unchanged."""
+    nv = _nv()
+    log("kv append", H, T, D, offset, t_new)
+    k0, _ = workloads.kv_cache(H, T, D, sinks=4)
+    gen = torch.Generator().manual_seed(H * 1000 + offset)
+    new = torch.randn(H, t_new, D, generator=gen)
+    new[:, 0, :3] *= 40.0  # beyond 2688 * s_g of the frozen scale: saturates
+    new = new.to(torch.bfloat16)
+    cache = nv.kv_quantize(k0.to(dev()))
+    before = [t.cpu().numpy().copy() for t in cache]
+    nv.kv_quantize_append(new.to(dev()), cache, offset)
+    torch.cuda.synchronize()
+    hs = before[2]
+    want_c, want_s = before[0].copy(), before[1].copy()
+    nb = workloads.bf16_bits(new)
+    for h in range(H):
+        oc, os_, _ = oracle.quantize(np.ascontiguousarray(nb[h]), s_g=np.float32(hs[h]))
+        want_c[h, offset:offset + t_new] = oc
+        want_s[h, offset:offset + t_new] = os_
+    got_c, got_s = cache[0].cpu().numpy(), cache[1].cpu().numpy()
+    assert np.array_equal(f32_bits(cache[2].cpu().numpy()), f32_bits(hs)), "head scales must not change"
+    assert np.array_equal(got_s, want_s), "%d scale bytes differ" % (got_s != want_s).sum()
+    assert np.array_equal(got_c, want_c), "%d code bytes differ" % (got_c != want_c).sum()
+    assert (want_s[:, offset] == 0x7E).any(), "the test should exercise saturation"
