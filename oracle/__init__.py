@@ -65,6 +65,8 @@ def _load():
                                c_p, c_i64, c_p, c_i64, c_p, c_p]),
         "orc_kv_quantize": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
         "orc_kv_dequantize": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i64, c_p]),
+        "orc_kv_attention": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_d,
+                                   c_p, c_i64, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -221,3 +223,29 @@ def kv_dequantize(codes, scales, head_scales):
     out = np.zeros((H, T, D), np.uint16)
     _check(_load().orc_kv_dequantize(_ptr(codes), _ptr(scales), _ptr(hs), H, T, D, _ptr(out)))
     return out
+
+
+def kv_attention(q, k_cache, v_cache, kv_tokens, scale, q_idx=None):
+    """Softmax attention of bf16 queries q (uint16 bits [H, Tq, D]) over the first
+    kv_tokens rows of the NVFP4 caches k_cache, v_cache = (codes [H, T, D/2],
+    scales [H, T, D/16], head_scales [H]); fp64 on the exact dequantized rows.
+
+    Returns (out, wabs), float64 [H, nq, D]: the attention output and
+    sum_j w_j |v_j| / sum_j w_j (q_idx selects the queries of every head)."""
+    q = np.ascontiguousarray(q)
+    if q.dtype != np.uint16 or q.ndim != 3:
+        raise OracleError("kv_attention expects uint16 bf16 bits [H, Tq, D]")
+    H, Tq, D = q.shape
+    kc, ks, kh = (np.ascontiguousarray(a) for a in k_cache)
+    vc, vs, vh = (np.ascontiguousarray(a) for a in v_cache)
+    T = kc.shape[1]
+    kh = np.ascontiguousarray(kh, np.float32)
+    vh = np.ascontiguousarray(vh, np.float32)
+    qi = None if q_idx is None else np.ascontiguousarray(q_idx, np.int64)
+    nq = Tq if qi is None else qi.size
+    out = np.zeros((H, nq, D), np.float64)
+    wabs = np.zeros((H, nq, D), np.float64)
+    _check(_load().orc_kv_attention(_ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kh), _ptr(vc), _ptr(vs), _ptr(vh),
+                                    T, kv_tokens, float(scale), None if qi is None else _ptr(qi), nq,
+                                    _ptr(out), _ptr(wabs)))
+    return out, wabs

@@ -328,3 +328,96 @@ int orc_kv_dequantize(const uint8_t *codes, const uint8_t *scales, const float *
   }
   return ORC_OK;
 }
+
+/* ---- attention over an NVFP4 KV cache ---------------------------------- */
+
+/* Exact dequantized cache row (val(q) val(s_b) s_g, <= 30 significant bits:
+ * exact in fp64). */
+static void decode_kv_row(const uint8_t *codes, const uint8_t *scales, float s_g, int64_t d, int64_t row,
+                          double *out) {
+  decode_row(codes, scales, d, row, out);
+  for (int64_t i = 0; i < d; i++) out[i] *= (double)s_g;
+}
+
+/* Softmax attention of bf16 queries over the first kv_tokens rows of an NVFP4
+ * K/V cache (the pages: the NVFP4 KV cache is restored by a parallel
+ * dequantization kernel and read by the attention).  For head h, query i:
+ *   s_j = scale * sum_d q[i][d] k[j][d],  w_j = exp(s_j - max_j s_j),
+ *   out[i][d]  = sum_j w_j v[j][d] / sum_j w_j,
+ *   wabs[i][d] = sum_j w_j |v[j][d]| / sum_j w_j,
+ * with k, v the exact dequantized rows; fp64 throughout, token order.  The
+ * cache is [heads][cache_tokens][...]; q and the outputs [heads][q_tokens or
+ * n_q][head_dim].  q_idx (n_q entries) restricts the queries of every head;
+ * NULL computes all q_tokens. */
+int orc_kv_attention(const uint16_t *q, int64_t heads, int64_t q_tokens, int64_t head_dim,
+                     const uint8_t *k_codes, const uint8_t *k_scales, const float *k_hs,
+                     const uint8_t *v_codes, const uint8_t *v_scales, const float *v_hs,
+                     int64_t cache_tokens, int64_t kv_tokens, double scale, const int64_t *q_idx,
+                     int64_t n_q, double *out, double *wabs) {
+  if (heads <= 0 || q_tokens < 0 || head_dim <= 0 || head_dim % 16 != 0 || kv_tokens <= 0 ||
+      kv_tokens > cache_tokens || !isfinite(scale))
+    return ORC_ERR_SHAPE;
+  const int64_t nq = q_idx ? n_q : q_tokens;
+  for (int64_t i = 0; i < nq; i++)
+    if (q_idx && (q_idx[i] < 0 || q_idx[i] >= q_tokens)) return ORC_ERR_SHAPE;
+  const int64_t D = head_dim, T = kv_tokens;
+  double *kd = (double *)malloc(sizeof(double) * (size_t)(T * D));
+  double *vd = (double *)malloc(sizeof(double) * (size_t)(T * D));
+  if (!kd || !vd) {
+    free(kd);
+    free(vd);
+    return ORC_ERR_SHAPE;
+  }
+  int fail = 0;
+  for (int64_t h = 0; h < heads && !fail; h++) {
+    const uint8_t *kc = k_codes + h * cache_tokens * (D / 2), *ks = k_scales + h * cache_tokens * (D / 16);
+    const uint8_t *vc = v_codes + h * cache_tokens * (D / 2), *vs = v_scales + h * cache_tokens * (D / 16);
+    for (int64_t j = 0; j < T; j++) {
+      decode_kv_row(kc, ks, k_hs[h], D, j, kd + j * D);
+      decode_kv_row(vc, vs, v_hs[h], D, j, vd + j * D);
+    }
+#pragma omp parallel reduction(| : fail)
+    {
+      double *s = (double *)malloc(sizeof(double) * (size_t)T);
+      double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+      if (!s || !qd) fail = 1;
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t ii = 0; ii < nq; ii++) {
+        if (!s || !qd) continue;
+        const int64_t i = q_idx ? q_idx[ii] : ii;
+        for (int64_t d = 0; d < D; d++) {
+          qd[d] = bf16_to_double(q[(h * q_tokens + i) * D + d]);
+          if (!isfinite(qd[d])) fail = 1;
+        }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < T; j++) {
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; d++) dot += qd[d] * kd[j * D + d];
+          s[j] = scale * dot;
+          if (s[j] > m) m = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < T; j++) {
+          s[j] = exp(s[j] - m);
+          l += s[j];
+        }
+        double *o = out + (h * nq + ii) * D, *wa = wabs + (h * nq + ii) * D;
+        for (int64_t d = 0; d < D; d++) o[d] = wa[d] = 0.0;
+        for (int64_t j = 0; j < T; j++)
+          for (int64_t d = 0; d < D; d++) {
+            o[d] += s[j] * vd[j * D + d];
+            wa[d] += s[j] * fabs(vd[j * D + d]);
+          }
+        for (int64_t d = 0; d < D; d++) {
+          o[d] /= l;
+          wa[d] /= l;
+        }
+      }
+      free(s);
+      free(qd);
+    }
+  }
+  free(kd);
+  free(vd);
+  return fail ? ORC_ERR_NONFINITE : ORC_OK;
+}
