@@ -243,6 +243,16 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     res["kv_cache_roundtrip"] = {"shape": [H, T, D], "tensors": 2, "ms": round(ms, 4),
                                  "GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (ms * 1e-3) / 1e9, 1),
                                  "bytes": n * (B_AMAX + B_ENCODE + B_DEQUANT)}
+    # attention of 4,096 new queries per head over the whole packed cache (K and V quantized above)
+    Tq = 4096
+    qa = workloads.attention_queries(H, Tq, D).to(dev)
+    oa = torch.empty_like(qa)
+    ms_a = time_calls(torch, lambda: nvfp4.kv_attention(qa, qk, qv, out=oa), 5, 2)
+    flop_a = 4.0 * H * Tq * T * D
+    res["kv_attention"] = {"heads": H, "q_tokens": Tq, "kv_tokens": T, "head_dim": D, "ms": round(ms_a, 4),
+                           "TFLOP/s": round(flop_a / (ms_a * 1e-3) / 1e12, 1),
+                           "frac_of_fp16_peak": round(flop_a / (ms_a * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
+    del qa, oa
     ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}

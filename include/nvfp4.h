@@ -184,6 +184,29 @@ nvfp4_status_t kv_dequantize(const uint8_t *codes, const uint8_t *scales, const 
                              int64_t heads, int64_t tokens, int64_t head_dim, void *kv_out,
                              void *stream);
 
+/*
+ * Softmax attention of bf16 queries over an NVFP4 KV cache, read packed:
+ *   q   [heads][q_tokens][head_dim] bf16,  out [heads][q_tokens][head_dim] bf16;
+ *   K, V caches as written by kv_quantize / kv_quantize_append:
+ *   codes [heads][cache_tokens][head_dim/2], scales [heads][cache_tokens]
+ *   [head_dim/16], per-head scales [heads]; the first kv_tokens rows of every
+ *   head are attended (no mask inside them):
+ *     out[h][i] = RN_bf16(sum_j w_j v_j / sum_j w_j),
+ *     w_j = exp(softmax_scale * (q_i . k_j) - max_j(...)),
+ *   k_j, v_j the dequantized rows val(q) val(s_b) s_g.  Computed with exact
+ *   bf16 / fp16 operands on the matrix cores, fp32 accumulation and an online
+ *   softmax; the probabilities are rounded to fp16 for the second product.
+ *   Per the d9249.github.io review (the NVFP4 KV cache is restored by a
+ *   parallel dequantization kernel for the attention) and the arXiv abstract
+ *   (NVFP4 KV cache).  Requires head_dim == 128, 1 <= kv_tokens <=
+ *   cache_tokens < 2^31, a finite softmax_scale; q_tokens == 0 is a no-op.
+ */
+nvfp4_status_t kv_attention(const void *q, int64_t heads, int64_t q_tokens, int64_t head_dim,
+                            const uint8_t *k_codes, const uint8_t *k_scales, const float *k_head_scales,
+                            const uint8_t *v_codes, const uint8_t *v_scales, const float *v_head_scales,
+                            int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, void *out,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

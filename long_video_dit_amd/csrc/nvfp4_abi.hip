@@ -9,6 +9,8 @@
 #include "../../include/nvfp4.h"
 #include "nvfp4_internal.h"
 
+#include <cmath>
+
 namespace nvfp4 {
 
 int device_cu_count() {
@@ -191,6 +193,26 @@ nvfp4_status_t kv_dequantize(const uint8_t* codes, const uint8_t* scales, const 
     return NVFP4_ERR_ALIGN;
   return from_hip(nvfp4::launch_dequant(codes, scales, head_scales, tokens * head_dim / 16, (int)heads, kv_out,
                                         nvfp4::kDtypeBf16, (hipStream_t)stream));
+}
+
+nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim, const uint8_t* k_codes,
+                            const uint8_t* k_scales, const float* k_head_scales, const uint8_t* v_codes,
+                            const uint8_t* v_scales, const float* v_head_scales, int64_t cache_tokens,
+                            int64_t kv_tokens, float softmax_scale, void* out, void* stream) {
+  if (head_dim != 128 || heads <= 0 || heads > 65535 || q_tokens < 0 || q_tokens >= (int64_t(1) << 31) ||
+      kv_tokens <= 0 || kv_tokens > cache_tokens || cache_tokens >= (int64_t(1) << 31) ||
+      heads > kMaxElems / (cache_tokens * head_dim) || (q_tokens > 0 && heads > kMaxElems / (q_tokens * head_dim)) ||
+      !std::isfinite(softmax_scale))
+    return NVFP4_ERR_SHAPE;
+  if (!k_head_scales || !v_head_scales || !k_codes || !k_scales || !v_codes || !v_scales ||
+      (q_tokens > 0 && (!q || !out)))
+    return NVFP4_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(k_head_scales, 4) || !aligned(v_head_scales, 4))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_kv_attention(q, k_codes, k_scales, k_head_scales, v_codes, v_scales, v_head_scales,
+                                             heads, q_tokens, cache_tokens, kv_tokens, softmax_scale, out,
+                                             (hipStream_t)stream));
 }
 
 }  // extern "C"

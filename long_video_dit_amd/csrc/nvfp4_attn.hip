@@ -1,0 +1,289 @@
+// Softmax attention of bf16 queries over an NVFP4 KV cache, for gfx950.
+//
+// The LongLive-2.0 pages restore the NVFP4 KV cache with a parallel
+// dequantization kernel for the attention (d9249.github.io review, "Core idea /
+// structure / operation"; arXiv abstract: the KV cache is held in NVFP4).
+// Here the attention reads the packed cache directly: each 64-token block of
+// K and V is decoded once per workgroup into LDS, exactly (a decoded element
+// val(q) * val(s) has at most 6 significant bits: exact in bf16 and fp16),
+// so HBM only carries the 0.5625 B/element of the packed cache.
+//
+//   o[h][i][:] = s_gV[h] * sum_j w_j v_j / sum_j w_j,
+//   w_j = exp(scale * s_gK[h] * (q_i . k_j) - max),  k_j, v_j without s_g.
+//
+// Per workgroup: 256 queries of one head (4 waves x 64, two MFMA column
+// tiles each).  Per block:
+//   S^T = K . Q^T   v_mfma_f32_32x32x16_bf16 (bf16 queries, exact bf16 K;
+//                   products exact in fp32), so each lane holds the scores of
+//                   ONE query (16 of a 32-token tile; the other 16 sit in lane
+//                   l ^ 32): the row maximum needs one cross-half exchange;
+//   online softmax  exp2 of scores pre-multiplied by scale * s_gK * log2(e),
+//                   running max m and per-lane partial sums l in fp32;
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_f16 (P rounded to fp16, exact fp16
+//                   V).  The A operand needs 8 consecutive tokens of one
+//                   head-dim column per lane while the cache is token-major:
+//                   two ds_read_b64_tr_b16 (transposing LDS reads) per operand
+//                   deliver them from V stored [token][d] in LDS.
+// The tokens of an MFMA k-step are ordered to match the score layout, so P
+// goes from the softmax to the MFMA without any exchange.
+//
+// LDS layouts (64 tokens x 256 B each, swizzled so that the decode writes,
+// the K operand reads and the transposing V reads are all bank-conflict
+// free):
+//   K  [token][16 slots of 16 B] bf16, chunk c (d = 8c..8c+7) in slot
+//      c ^ (token % 16);
+//   V  [token][32 slots of 8 B] fp16, chunk c (d = 4c..4c+3) in slot
+//      c ^ (8 (token % 4) + 2 ((token / 4) % 4)).
+#include <hip/hip_runtime.h>
+
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __fp16 fp16x4_raw __attribute__((__vector_size__(8)));  // operand type of the transposing read
+typedef __attribute__((address_space(3))) fp16x4_raw lds_fp16x4;
+
+constexpr int kAD = 128;         // head_dim
+constexpr int kABN = 64;         // cache tokens per block
+constexpr int kAQW = 64;         // queries per wave
+constexpr int kABM = 4 * kAQW;   // queries per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnSmem {
+  uint8_t k[kABN * 256];
+  uint8_t v[kABN * 256];
+};
+
+// Packed codes and scale bytes of one token and one quarter of head_dim
+// (d = 32 qd .. 32 qd + 31) of K and of V: thread tid takes token tid % 64 of
+// the block and quarter tid / 64.
+struct RawKV {
+  u32x4 kc, vc;
+  uint32_t ks, vs;
+};
+
+__device__ __forceinline__ void load_raw(RawKV& r, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
+                                         const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int64_t tok,
+                                         int qd) {
+  r.kc = *reinterpret_cast<const u32x4*>(kc + tok * (kAD / 2) + 16 * qd);
+  r.vc = *reinterpret_cast<const u32x4*>(vc + tok * (kAD / 2) + 16 * qd);
+  r.ks = *reinterpret_cast<const uint16_t*>(ks + tok * (kAD / 16) + 2 * qd);
+  r.vs = *reinterpret_cast<const uint16_t*>(vs + tok * (kAD / 16) + 2 * qd);
+}
+
+__device__ __forceinline__ uint32_t word_at(const u32x4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Codes of byte P of w times the block scale: two exact bf16 (K) or fp16 (V).
+template <int P>
+__device__ __forceinline__ uint32_t k_pair(uint32_t w, float sv) {
+  const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, P);
+  const bf16x2 b = {(__bf16)(f.x * sv), (__bf16)(f.y * sv)};
+  return __builtin_bit_cast(uint32_t, b);
+}
+template <int P>
+__device__ __forceinline__ uint32_t v_pair(uint32_t w, f16x2 sv) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, P) * sv);
+}
+
+// Decode the thread's 32 K and 32 V elements into LDS (exact bf16 / fp16).
+__device__ __forceinline__ void decode_to_lds(const RawKV& r, AttnSmem& sm, int t, int qd) {
+#pragma unroll
+  for (int wi = 0; wi < 4; wi++) {  // 8 elements d = 32 qd + 8 wi + (0..7), block 2 qd + wi / 2
+    const uint32_t kb = (r.ks >> (8 * (wi >> 1))) & 0xffu;
+    const float ksv = e4m3_value(kb);
+    const uint32_t kw = word_at(r.kc, wi);
+    const uint32_t kp[4] = {k_pair<0>(kw, ksv), k_pair<1>(kw, ksv), k_pair<2>(kw, ksv), k_pair<3>(kw, ksv)};
+    const int kslot = (4 * qd + wi) ^ (t & 15);
+    *reinterpret_cast<u32x4*>(sm.k + t * 256 + kslot * 16) = u32x4{kp[0], kp[1], kp[2], kp[3]};
+
+    const uint32_t vb = (r.vs >> (8 * (wi >> 1))) & 0xffu;
+    const f16x2 vsv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vb | (vb << 8), 1.0f, false);
+    const uint32_t vw = word_at(r.vc, wi);
+    const uint32_t vp[4] = {v_pair<0>(vw, vsv), v_pair<1>(vw, vsv), v_pair<2>(vw, vsv), v_pair<3>(vw, vsv)};
+    const int vslot = (8 * qd + 2 * wi) ^ (8 * (t & 3) + 2 * ((t >> 2) & 3));  // even: two adjacent 8-B slots
+    *reinterpret_cast<u32x4*>(sm.v + t * 256 + vslot * 8) = u32x4{vp[0], vp[1], vp[2], vp[3]};
+  }
+}
+
+// A operand of S^T = K . Q^T for token tile tau, k-step s: this lane's token
+// 32 tau + lane % 32, head-dim 16 s + 8 (lane / 32) .. + 7.
+__device__ __forceinline__ bf16x8 k_frag(const AttnSmem& sm, int tau, int s, int lane) {
+  const int tok = 32 * tau + (lane & 31);
+  const int slot = (2 * s + (lane >> 5)) ^ (tok & 15);
+  return *reinterpret_cast<const bf16x8*>(sm.k + tok * 256 + slot * 16);
+}
+
+// A operand of O^T = V^T . P^T for head-dim tile dt and k-step (tau, nu):
+// lane l gets head-dim 32 dt + l % 32 and the 8 tokens of k = 8 (l / 32) + i,
+// token(i) = 32 tau + 16 nu + 8 (i / 4) + 4 (l / 32) + i % 4 (the order in
+// which the score layout holds them).  Each of the two transposing reads
+// covers i = 4c .. 4c + 3: within a group of 16 lanes, lane i gets element
+// i % 4 of the 8-byte chunks addressed by lanes i / 4 + 4 j (j = 0..3), so
+// lane s of the group addresses token(4c + s / 4), head-dim chunk
+// 8 dt + 4 ((l / 16) % 2) + s % 4.
+__device__ __forceinline__ f16x8 v_frag(const AttnSmem& sm, int dt, int tau, int nu, int lane) {
+  const int hh = lane >> 5, g = (lane >> 4) & 1, s16 = lane & 15;
+  const int q = s16 & 3, j = s16 >> 2;
+  f16x4 part[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const int tok = 32 * tau + 16 * nu + 8 * c + 4 * hh + j;
+    const int chunk = 8 * dt + 4 * g + q;
+    const int slot = chunk ^ (8 * j + 2 * ((2 * c + hh) & 3));  // tok % 4 == j, (tok / 4) % 4 == (2c + hh) % 4
+    part[c] = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                            (lds_fp16x4*)((__attribute__((address_space(3))) uint8_t*)sm.v +
+                                                          tok * 256 + slot * 8)));
+  }
+  return f16x8{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+}
+
+__global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
+    const __bf16* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    const float* __restrict__ k_hs, const uint8_t* __restrict__ v_codes, const uint8_t* __restrict__ v_scales,
+    const float* __restrict__ v_hs, int q_tokens, int64_t cache_tokens, int kv_tokens, float scale,
+    __bf16* __restrict__ out) {
+  __shared__ AttnSmem sm;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int64_t cache_row0 = (int64_t)h * cache_tokens;
+  const uint8_t* kc = k_codes + cache_row0 * (kAD / 2);
+  const uint8_t* ks = k_scales + cache_row0 * (kAD / 16);
+  const uint8_t* vc = v_codes + cache_row0 * (kAD / 2);
+  const uint8_t* vs = v_scales + cache_row0 * (kAD / 16);
+  const float c_k = scale * k_hs[h] * kLog2e;  // raw dot product -> log2 units
+  const float s_gv = v_hs[h];
+
+  // Queries of this wave: two column tiles of 32; rows past q_tokens repeat the last row.
+  const int qbase = blockIdx.x * kABM + wave * kAQW;
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const int qi = min(qbase + 32 * qt + n, q_tokens - 1);
+    const __bf16* qrow = q + ((int64_t)h * q_tokens + qi) * kAD;
+#pragma unroll
+    for (int s = 0; s < 8; s++) qf[qt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+  }
+
+  f32x16 oacc[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) oacc[qt][dt] = f32x16{};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+
+  const int t_dec = threadIdx.x & 63, qd_dec = threadIdx.x >> 6;
+  const int nblk = (kv_tokens + kABN - 1) / kABN;
+  RawKV raw;
+  load_raw(raw, kc, ks, vc, vs, min(t_dec, kv_tokens - 1), qd_dec);
+
+  for (int blk = 0; blk < nblk; blk++) {
+    __syncthreads();  // the previous block's LDS reads are done
+    decode_to_lds(raw, sm, t_dec, qd_dec);
+    if (blk + 1 < nblk) load_raw(raw, kc, ks, vc, vs, min((blk + 1) * kABN + t_dec, kv_tokens - 1), qd_dec);
+    __syncthreads();
+
+    // S^T = K . Q^T: sacc[tau][qt], lane (query n, half hh), element e ->
+    // token 32 tau + 8 (e / 4) + 4 hh + e % 4.
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int tau = 0; tau < 2; tau++) {
+      sacc[tau][0] = f32x16{};
+      sacc[tau][1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; s++) {
+        const bf16x8 kf = k_frag(sm, tau, s, lane);
+        sacc[tau][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][s], sacc[tau][0], 0, 0, 0);
+        sacc[tau][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][s], sacc[tau][1], 0, 0, 0);
+      }
+    }
+
+    const bool last = blk + 1 == nblk;
+    f16x8 pf[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++) {
+      float t[32];
+#pragma unroll
+      for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+          float x = sacc[tau][qt][e] * c_k;
+          if (last && blk * kABN + 32 * tau + 8 * (e >> 2) + 4 * hh + (e & 3) >= kv_tokens) x = -INFINITY;
+          t[16 * tau + e] = x;
+        }
+      float bm = t[0];
+#pragma unroll
+      for (int i = 1; i < 32; i++) bm = fmaxf(bm, t[i]);
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m[qt], bm);
+      const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        t[i] = __builtin_amdgcn_exp2f(t[i] - m_new);
+        sum += t[i];
+      }
+      l[qt] = l[qt] * alpha + sum;
+      m[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) oacc[qt][dt] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {  // k-step u: tile u / 2, elements 8 (u % 2) .. + 7
+        const float* p = t + 16 * (u >> 1) + 8 * (u & 1);
+        pf[qt][u] = f16x8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                          (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+      }
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const f16x8 vf = v_frag(sm, dt, u >> 1, u & 1, lane);
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[0][u], oacc[0][dt], 0, 0, 0);
+        oacc[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[1][u], oacc[1][dt], 0, 0, 0);
+      }
+  }
+
+  // o = s_gV * O / l, l = this lane's partial sum + the other half's.
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const float lt = l[qt] + __shfl_xor(l[qt], 32);
+    const float inv = s_gv / lt;
+    const int qi = qbase + 32 * qt + n;
+    if (qi >= q_tokens) continue;
+    __bf16* orow = out + ((int64_t)h * q_tokens + qi) * kAD;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int eg = 0; eg < 4; eg++) {  // head-dim 32 dt + 8 eg + 4 hh + (0..3)
+        const f32x16& a = oacc[qt][dt];
+        const bf16x2 p0 = {(__bf16)(a[4 * eg] * inv), (__bf16)(a[4 * eg + 1] * inv)};
+        const bf16x2 p1 = {(__bf16)(a[4 * eg + 2] * inv), (__bf16)(a[4 * eg + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * eg + 4 * hh) =
+            u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint8_t* k_scales, const float* k_hs,
+                               const uint8_t* v_codes, const uint8_t* v_scales, const float* v_hs, int64_t heads,
+                               int64_t q_tokens, int64_t cache_tokens, int64_t kv_tokens, float scale, void* out,
+                               hipStream_t stream) {
+  if (q_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)((q_tokens + kABM - 1) / kABM), (unsigned)heads);
+  return launch_kernel(attn_nvfp4_kv_kernel, grid, dim3(256), 0, stream, (const __bf16*)q, k_codes, k_scales, k_hs,
+                       v_codes, v_scales, v_hs, (int)q_tokens, cache_tokens, (int)kv_tokens, scale, (__bf16*)out);
+}
+
+}  // namespace nvfp4

@@ -46,6 +46,12 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
                           int groups, void* y, int y_dtype, hipStream_t stream);
 
+// Attention over an NVFP4 KV cache (nvfp4_attn.hip), head_dim 128.
+hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint8_t* k_scales, const float* k_hs,
+                               const uint8_t* v_codes, const uint8_t* v_scales, const float* v_hs, int64_t heads,
+                               int64_t q_tokens, int64_t cache_tokens, int64_t kv_tokens, float scale, void* out,
+                               hipStream_t stream);
+
 // W4A4 GEMM launcher (nvfp4_gemm.hip).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_sg, int64_t M, int64_t N, int64_t K, void* c,

@@ -29,6 +29,7 @@ SIGNATURES = {
     "kv_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kv_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P]),
+    "kv_attention": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P]),
 }
 
 _lib = None
@@ -183,3 +184,19 @@ def kv_dequantize(codes, scales, head_scales, out=None):
     y = torch.empty(H, T, D, dtype=torch.bfloat16, device=codes.device) if out is None else out
     _call("kv_dequantize", _ptr(codes), _ptr(scales), _ptr(head_scales), H, T, D, _ptr(y), _stream(codes.device))
     return y
+
+
+def kv_attention(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None):
+    """Softmax attention of q bf16 [H, Tq, D] over the first kv_tokens rows of the NVFP4 caches
+    k_cache, v_cache = (codes [H, T, D/2], scales [H, T, D/16], head_scales [H]); bf16 [H, Tq, D]."""
+    _need_cuda(q, *k_cache, *v_cache)
+    H, Tq, D = q.shape
+    kc, ks, kh = k_cache
+    vc, vs, vh = v_cache
+    T = kc.shape[1]
+    kv_tokens = T if kv_tokens is None else kv_tokens
+    scale = D ** -0.5 if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    _call("kv_attention", _ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kh), _ptr(vc), _ptr(vs), _ptr(vh), T, kv_tokens,
+          float(scale), _ptr(o), _stream(q.device))
+    return o

@@ -100,6 +100,14 @@ def test_validation_errors_launch_nothing():
     assert lib.kv_quantize_append(None, 4, 16, 128, buf, buf, buf, 64, 0, None) == nv.ERR_NULL
     assert lib.kv_quantize_append(buf, 4, 16, 128, buf, odd, buf, 64, 0, None) == nv.ERR_ALIGN
     assert lib.kv_quantize_append(buf, 4, 0, 128, buf, buf, buf, 64, 64, None) == nv.OK  # empty append
+    kva = lambda *a: lib.kv_attention(*a)
+    assert kva(buf, 2, 8, 64, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_SHAPE  # head_dim 128
+    assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 33, 0.1, buf, None) == nv.ERR_SHAPE  # > cache
+    assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 0, 0.1, buf, None) == nv.ERR_SHAPE
+    assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, float("nan"), buf, None) == nv.ERR_SHAPE
+    assert kva(buf, 2, 8, 128, buf, buf, None, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_NULL
+    assert kva(None, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_NULL
+    assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, odd, None) == nv.ERR_ALIGN
     assert lib.kv_dequantize(buf, buf, buf, 4, -1, 128, buf, None) == nv.ERR_SHAPE
     assert lib.kv_dequantize(buf, buf, buf, 4, 16, 128, odd, None) == nv.ERR_ALIGN
 

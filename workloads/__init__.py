@@ -18,7 +18,8 @@ torch.Generator seeded 1000*cfg + t, t = 0 activations/K, 1 weights/V,
   4  A bf16 [16384, 14336] = GELU(N(0, 1)) (erf form, fp32);
      W bf16 [3072, 14336] ~ N(0, 0.01)
   5  K, V bf16 [24, 65536, 128] ~ N(0, 1), tokens 0..3 of every head x8
-     (attention-sink tokens)
+     (attention-sink tokens); queries of a new chunk attending that cache
+     bf16 [24, 4096, 128] ~ N(0, 1) (t = 2)
 Sizes can be overridden (same recipe) for small parity cases.
 """
 import torch
@@ -83,6 +84,11 @@ def kv_cache(H=None, T=None, D=None, sinks=4):
         x[:, :sinks, :] *= 8.0
         out.append(x.to(torch.bfloat16))
     return tuple(out)
+
+
+def attention_queries(H=24, Tq=4096, D=128):
+    """Queries of a new chunk attending the NVFP4 KV cache: bf16 [H, Tq, D] ~ N(0, 1), seed 1000 * 5 + 2."""
+    return torch.randn(H, Tq, D, generator=generator(5, 2)).to(torch.bfloat16)
 
 
 def bf16_bits(t):
