@@ -144,12 +144,62 @@ __device__ __forceinline__ f16x8 v_frag(const AttnSmem& sm, int dt, int tau, int
   return f16x8{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
 }
 
+// Online softmax of one query tile for one block: scores s (2 token tiles x
+// 16 per lane), running max m (log2 units) and sum l; returns the fp16
+// probabilities as the B operands of the 4 k-steps of O^T += V^T P^T and the
+// rescale factor of O.  The row sum is taken over the fp16 probabilities
+// (v_dot2), the same values the second product uses.
+__device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], float c, bool masked, int valid_from_lane,
+                                              int hh, float& m, float& l, f16x8 (&pf)[4]) {
+  // block maximum of c * s over the valid tokens (c >= 0: max of s, else min)
+  const float inf = c >= 0.0f ? -INFINITY : INFINITY;
+  float r[32];
+#pragma unroll
+  for (int tau = 0; tau < 2; tau++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const int tok = 32 * tau + 8 * (e >> 2) + 4 * hh + (e & 3);
+      r[16 * tau + e] = (masked && tok >= valid_from_lane) ? inf : s[tau][e];
+    }
+  float bm;
+  if (c >= 0.0f) {
+    bm = r[0];
+#pragma unroll
+    for (int i = 1; i < 32; i++) bm = fmaxf(bm, r[i]);
+  } else {
+    bm = r[0];
+#pragma unroll
+    for (int i = 1; i < 32; i++) bm = fminf(bm, r[i]);
+  }
+  bm *= c;
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(m, bm);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  m = m_new;
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {  // k-step u: token tile u / 2, elements 8 (u % 2) .. + 7
+    f16x2 h2[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int e0 = 16 * (u >> 1) + 8 * (u & 1) + 2 * i;
+      const float t0 = masked && r[e0] == inf ? -INFINITY : __builtin_fmaf(r[e0], c, -m_new);
+      const float t1 = masked && r[e0 + 1] == inf ? -INFINITY : __builtin_fmaf(r[e0 + 1], c, -m_new);
+      h2[i] = f16x2{(_Float16)__builtin_amdgcn_exp2f(t0), (_Float16)__builtin_amdgcn_exp2f(t1)};
+      sum = __builtin_amdgcn_fdot2(h2[i], f16x2{(_Float16)1.0f, (_Float16)1.0f}, sum, false);
+    }
+    pf[u] = f16x8{h2[0].x, h2[0].y, h2[1].x, h2[1].y, h2[2].x, h2[2].y, h2[3].x, h2[3].y};
+  }
+  l = l * alpha + sum;
+  return alpha;
+}
+
 __global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const float* __restrict__ k_hs, const uint8_t* __restrict__ v_codes, const uint8_t* __restrict__ v_scales,
     const float* __restrict__ v_hs, int q_tokens, int64_t cache_tokens, int kv_tokens, float scale,
     __bf16* __restrict__ out) {
-  __shared__ AttnSmem sm;
+  __shared__ AttnSmem sm[2];
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -179,78 +229,68 @@ __global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
     for (int dt = 0; dt < 4; dt++) oacc[qt][dt] = f32x16{};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
 
+  // Block 0 decoded into sm[0], block 1 prefetched into registers.
   const int t_dec = threadIdx.x & 63, qd_dec = threadIdx.x >> 6;
   const int nblk = (kv_tokens + kABN - 1) / kABN;
   RawKV raw;
   load_raw(raw, kc, ks, vc, vs, min(t_dec, kv_tokens - 1), qd_dec);
+  decode_to_lds(raw, sm[0], t_dec, qd_dec);
+  if (nblk > 1) load_raw(raw, kc, ks, vc, vs, min(kABN + t_dec, kv_tokens - 1), qd_dec);
+  __syncthreads();
 
   for (int blk = 0; blk < nblk; blk++) {
-    __syncthreads();  // the previous block's LDS reads are done
-    decode_to_lds(raw, sm, t_dec, qd_dec);
-    if (blk + 1 < nblk) load_raw(raw, kc, ks, vc, vs, min((blk + 1) * kABN + t_dec, kv_tokens - 1), qd_dec);
-    __syncthreads();
-
-    // S^T = K . Q^T: sacc[tau][qt], lane (query n, half hh), element e ->
+    const AttnSmem& cur = sm[blk & 1];
+    // S^T = K . Q^T: sacc[qt][tau], lane (query n, half hh), element e ->
     // token 32 tau + 8 (e / 4) + 4 hh + e % 4.
     f32x16 sacc[2][2];
 #pragma unroll
-    for (int tau = 0; tau < 2; tau++) {
-      sacc[tau][0] = f32x16{};
-      sacc[tau][1] = f32x16{};
+    for (int qt = 0; qt < 2; qt++) sacc[qt][0] = sacc[qt][1] = f32x16{};
+    {
+      // K operands read two k-steps ahead of their MFMAs
+      bf16x8 kf[3];
+      kf[0] = k_frag(cur, 0, 0, lane);
+      kf[1] = k_frag(cur, 0, 1, lane);
 #pragma unroll
-      for (int s = 0; s < 8; s++) {
-        const bf16x8 kf = k_frag(sm, tau, s, lane);
-        sacc[tau][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][s], sacc[tau][0], 0, 0, 0);
-        sacc[tau][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][s], sacc[tau][1], 0, 0, 0);
+      for (int st = 0; st < 16; st++) {
+        const int tau = st >> 3, s = st & 7;
+        if (st + 2 < 16) kf[(st + 2) % 3] = k_frag(cur, (st + 2) >> 3, (st + 2) & 7, lane);
+        sacc[0][tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st % 3], qf[0][s], sacc[0][tau], 0, 0, 0);
+        sacc[1][tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st % 3], qf[1][s], sacc[1][tau], 0, 0, 0);
       }
     }
 
-    const bool last = blk + 1 == nblk;
+    const bool masked = blk + 1 == nblk && kv_tokens % kABN != 0;
+    const int valid = kv_tokens - blk * kABN;
     f16x8 pf[2][4];
 #pragma unroll
     for (int qt = 0; qt < 2; qt++) {
-      float t[32];
+      const float alpha = softmax_tile(sacc[qt], c_k, masked, valid, hh, m[qt], l[qt], pf[qt]);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // the running max moved for some query
 #pragma unroll
-      for (int tau = 0; tau < 2; tau++)
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-          float x = sacc[tau][qt][e] * c_k;
-          if (last && blk * kABN + 32 * tau + 8 * (e >> 2) + 4 * hh + (e & 3) >= kv_tokens) x = -INFINITY;
-          t[16 * tau + e] = x;
-        }
-      float bm = t[0];
-#pragma unroll
-      for (int i = 1; i < 32; i++) bm = fmaxf(bm, t[i]);
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m[qt], bm);
-      const float alpha = __builtin_amdgcn_exp2f(m[qt] - m_new);
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; i++) {
-        t[i] = __builtin_amdgcn_exp2f(t[i] - m_new);
-        sum += t[i];
+        for (int dt = 0; dt < 4; dt++) oacc[qt][dt] *= alpha;
       }
-      l[qt] = l[qt] * alpha + sum;
-      m[qt] = m_new;
+    }
+    // O^T += V^T . P^T: each V operand serves both query tiles; operands are
+    // read one k-step ahead of their MFMAs.
+    {
+      f16x8 vf[2];
+      vf[0] = v_frag(cur, 0, 0, 0, lane);
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) oacc[qt][dt] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; u++) {  // k-step u: tile u / 2, elements 8 (u % 2) .. + 7
-        const float* p = t + 16 * (u >> 1) + 8 * (u & 1);
-        pf[qt][u] = f16x8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
-                          (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+      for (int st = 0; st < 16; st++) {
+        const int dt = st >> 2, u = st & 3;
+        if (st + 1 < 16) vf[(st + 1) & 1] = v_frag(cur, (st + 1) >> 2, ((st + 1) & 3) >> 1, (st + 1) & 1, lane);
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1], pf[0][u], oacc[0][dt], 0, 0, 0);
+        oacc[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1], pf[1][u], oacc[1][dt], 0, 0, 0);
       }
     }
 
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const f16x8 vf = v_frag(sm, dt, u >> 1, u & 1, lane);
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[0][u], oacc[0][dt], 0, 0, 0);
-        oacc[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[1][u], oacc[1][dt], 0, 0, 0);
-      }
+    // Next block: decode into the other LDS buffer (its last readers finished
+    // before the previous barrier), prefetch the one after.
+    if (blk + 1 < nblk) {
+      decode_to_lds(raw, sm[(blk + 1) & 1], t_dec, qd_dec);
+      if (blk + 2 < nblk) load_raw(raw, kc, ks, vc, vs, min((blk + 2) * kABN + t_dec, kv_tokens - 1), qd_dec);
+    }
+    __syncthreads();
   }
 
   // o = s_gV * O / l, l = this lane's partial sum + the other half's.
