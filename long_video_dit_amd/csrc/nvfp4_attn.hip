@@ -11,8 +11,9 @@
 //   o[h][i][:] = s_gV[h] * sum_j w_j v_j / sum_j w_j,
 //   w_j = exp(scale * s_gK[h] * (q_i . k_j) - max),  k_j, v_j without s_g.
 //
-// Per workgroup: 256 queries of one head (4 waves x 64, two MFMA column
-// tiles each).  Per block:
+// Per workgroup: 256 queries of one head (8 waves x 32, one MFMA column tile
+// each; two waves per SIMD, so one wave's softmax overlaps the other's
+// MFMAs).  Per block:
 //   S^T = K . Q^T   v_mfma_f32_32x32x16_bf16 (bf16 queries, exact bf16 K;
 //                   products exact in fp32), so each lane holds the scores of
 //                   ONE query (16 of a 32-token tile; the other 16 sit in lane
@@ -50,8 +51,9 @@ typedef __attribute__((address_space(3))) fp16x4_raw lds_fp16x4;
 
 constexpr int kAD = 128;         // head_dim
 constexpr int kABN = 64;         // cache tokens per block
-constexpr int kAQW = 64;         // queries per wave
-constexpr int kABM = 4 * kAQW;   // queries per workgroup
+constexpr int kAQW = 32;         // queries per wave
+constexpr int kAW = 8;           // waves per workgroup
+constexpr int kABM = kAW * kAQW; // queries per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnSmem {
@@ -59,25 +61,21 @@ struct AttnSmem {
   uint8_t v[kABN * 256];
 };
 
-// Packed codes and scale bytes of one token and one quarter of head_dim
-// (d = 32 qd .. 32 qd + 31) of K and of V: thread tid takes token tid % 64 of
-// the block and quarter tid / 64.
+// Packed codes and scale byte of one token and one NVFP4 block of head_dim
+// (d = 16 qd .. 16 qd + 15) of K and of V: thread tid takes token tid % 64 of
+// the cache block and qd = tid / 64.
 struct RawKV {
-  u32x4 kc, vc;
+  u32x2 kc, vc;
   uint32_t ks, vs;
 };
 
 __device__ __forceinline__ void load_raw(RawKV& r, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
                                          const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int64_t tok,
                                          int qd) {
-  r.kc = *reinterpret_cast<const u32x4*>(kc + tok * (kAD / 2) + 16 * qd);
-  r.vc = *reinterpret_cast<const u32x4*>(vc + tok * (kAD / 2) + 16 * qd);
-  r.ks = *reinterpret_cast<const uint16_t*>(ks + tok * (kAD / 16) + 2 * qd);
-  r.vs = *reinterpret_cast<const uint16_t*>(vs + tok * (kAD / 16) + 2 * qd);
-}
-
-__device__ __forceinline__ uint32_t word_at(const u32x4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+  r.kc = *reinterpret_cast<const u32x2*>(kc + tok * (kAD / 2) + 8 * qd);
+  r.vc = *reinterpret_cast<const u32x2*>(vc + tok * (kAD / 2) + 8 * qd);
+  r.ks = ks[tok * (kAD / 16) + qd];
+  r.vs = vs[tok * (kAD / 16) + qd];
 }
 
 // Codes of byte P of w times the block scale: two exact bf16 (K) or fp16 (V).
@@ -92,22 +90,20 @@ __device__ __forceinline__ uint32_t v_pair(uint32_t w, f16x2 sv) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, P) * sv);
 }
 
-// Decode the thread's 32 K and 32 V elements into LDS (exact bf16 / fp16).
+// Decode the thread's 16 K and 16 V elements into LDS (exact bf16 / fp16).
 __device__ __forceinline__ void decode_to_lds(const RawKV& r, AttnSmem& sm, int t, int qd) {
+  const float ksv = e4m3_value(r.ks);
+  const f16x2 vsv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs | (r.vs << 8), 1.0f, false);
 #pragma unroll
-  for (int wi = 0; wi < 4; wi++) {  // 8 elements d = 32 qd + 8 wi + (0..7), block 2 qd + wi / 2
-    const uint32_t kb = (r.ks >> (8 * (wi >> 1))) & 0xffu;
-    const float ksv = e4m3_value(kb);
-    const uint32_t kw = word_at(r.kc, wi);
+  for (int wi = 0; wi < 2; wi++) {  // 8 elements d = 16 qd + 8 wi + (0..7)
+    const uint32_t kw = wi ? r.kc.y : r.kc.x;
     const uint32_t kp[4] = {k_pair<0>(kw, ksv), k_pair<1>(kw, ksv), k_pair<2>(kw, ksv), k_pair<3>(kw, ksv)};
-    const int kslot = (4 * qd + wi) ^ (t & 15);
+    const int kslot = (2 * qd + wi) ^ (t & 15);
     *reinterpret_cast<u32x4*>(sm.k + t * 256 + kslot * 16) = u32x4{kp[0], kp[1], kp[2], kp[3]};
 
-    const uint32_t vb = (r.vs >> (8 * (wi >> 1))) & 0xffu;
-    const f16x2 vsv = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vb | (vb << 8), 1.0f, false);
-    const uint32_t vw = word_at(r.vc, wi);
+    const uint32_t vw = wi ? r.vc.y : r.vc.x;
     const uint32_t vp[4] = {v_pair<0>(vw, vsv), v_pair<1>(vw, vsv), v_pair<2>(vw, vsv), v_pair<3>(vw, vsv)};
-    const int vslot = (8 * qd + 2 * wi) ^ (8 * (t & 3) + 2 * ((t >> 2) & 3));  // even: two adjacent 8-B slots
+    const int vslot = (4 * qd + 2 * wi) ^ (8 * (t & 3) + 2 * ((t >> 2) & 3));  // even: two adjacent 8-B slots
     *reinterpret_cast<u32x4*>(sm.v + t * 256 + vslot * 8) = u32x4{vp[0], vp[1], vp[2], vp[3]};
   }
 }
@@ -147,54 +143,92 @@ __device__ __forceinline__ f16x8 v_frag(const AttnSmem& sm, int dt, int tau, int
 // Online softmax of one query tile for one block: scores s (2 token tiles x
 // 16 per lane), running max m (log2 units) and sum l; returns the fp16
 // probabilities as the B operands of the 4 k-steps of O^T += V^T P^T and the
-// rescale factor of O.  The row sum is taken over the fp16 probabilities
-// (v_dot2), the same values the second product uses.
-__device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], float c, bool masked, int valid_from_lane,
-                                              int hh, float& m, float& l, f16x8 (&pf)[4]) {
-  // block maximum of c * s over the valid tokens (c >= 0: max of s, else min)
-  const float inf = c >= 0.0f ? -INFINITY : INFINITY;
-  float r[32];
-#pragma unroll
-  for (int tau = 0; tau < 2; tau++)
-#pragma unroll
-    for (int e = 0; e < 16; e++) {
-      const int tok = 32 * tau + 8 * (e >> 2) + 4 * hh + (e & 3);
-      r[16 * tau + e] = (masked && tok >= valid_from_lane) ? inf : s[tau][e];
-    }
-  float bm;
+// rescale factor of O.  Tokens from `valid` on lie past the end of the cache:
+// their LDS rows repeat the last cached token, so they cannot move the
+// maximum, and their probabilities are zeroed (only in a ragged last block)
+// before the row sum, which is taken over the fp16 probabilities (v_dot2),
+// the same values the second product uses.
+__device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], float c, int valid, int hh, float& m, float& l,
+                                              f16x8 (&pf)[4]) {
+  // block maximum of c * s (c >= 0: c * max s, else c * min s)
+  float bm = s[0][0];
   if (c >= 0.0f) {
-    bm = r[0];
 #pragma unroll
-    for (int i = 1; i < 32; i++) bm = fmaxf(bm, r[i]);
+    for (int i = 1; i < 32; i++) bm = fmaxf(bm, s[i >> 4][i & 15]);
   } else {
-    bm = r[0];
 #pragma unroll
-    for (int i = 1; i < 32; i++) bm = fminf(bm, r[i]);
+    for (int i = 1; i < 32; i++) bm = fminf(bm, s[i >> 4][i & 15]);
   }
   bm *= c;
   bm = fmaxf(bm, __shfl_xor(bm, 32));
   const float m_new = fmaxf(m, bm);
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
   m = m_new;
-  float sum = 0.0f;
 #pragma unroll
   for (int u = 0; u < 4; u++) {  // k-step u: token tile u / 2, elements 8 (u % 2) .. + 7
-    f16x2 h2[4];
+    const f32x16& st = s[u >> 1];
+    _Float16 p[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int e0 = 16 * (u >> 1) + 8 * (u & 1) + 2 * i;
-      const float t0 = masked && r[e0] == inf ? -INFINITY : __builtin_fmaf(r[e0], c, -m_new);
-      const float t1 = masked && r[e0 + 1] == inf ? -INFINITY : __builtin_fmaf(r[e0 + 1], c, -m_new);
-      h2[i] = f16x2{(_Float16)__builtin_amdgcn_exp2f(t0), (_Float16)__builtin_amdgcn_exp2f(t1)};
-      sum = __builtin_amdgcn_fdot2(h2[i], f16x2{(_Float16)1.0f, (_Float16)1.0f}, sum, false);
-    }
-    pf[u] = f16x8{h2[0].x, h2[0].y, h2[1].x, h2[1].y, h2[2].x, h2[2].y, h2[3].x, h2[3].y};
+    for (int i = 0; i < 8; i++) p[i] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * (u & 1) + i], c, -m_new));
+    pf[u] = f16x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]};
   }
+  if (valid < kABN) {
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int e = 8 * (u & 1) + i;
+        const int tok = 32 * (u >> 1) + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (tok >= valid) pf[u][i] = (_Float16)0.0f;
+      }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      sum = __builtin_amdgcn_fdot2(f16x2{pf[u][2 * i], pf[u][2 * i + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, sum,
+                                   false);
   l = l * alpha + sum;
   return alpha;
 }
 
-__global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
+// One cache block (in LDS) against the wave's 32 queries: S^T = K . Q^T,
+// online softmax, O^T += V^T . P^T.
+__device__ __forceinline__ void attn_block(const AttnSmem& cur, const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& m,
+                                           float& l, float c_k, int valid, int lane) {
+  // S^T = K . Q^T: sacc[tau], lane (query n, half hh), element e ->
+  // token 32 tau + 8 (e / 4) + 4 hh + e % 4.
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  {
+    // K operands read two k-steps ahead of their MFMAs
+    bf16x8 kf[3];
+    kf[0] = k_frag(cur, 0, 0, lane);
+    kf[1] = k_frag(cur, 0, 1, lane);
+#pragma unroll
+    for (int st = 0; st < 16; st++) {
+      if (st + 2 < 16) kf[(st + 2) % 3] = k_frag(cur, (st + 2) >> 3, (st + 2) & 7, lane);
+      sacc[st >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st % 3], qf[st & 7], sacc[st >> 3], 0, 0, 0);
+    }
+  }
+
+  f16x8 pf[4];
+  const float alpha = softmax_tile(sacc, c_k, valid, lane >> 5, m, l, pf);
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // the running max moved for some query
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) oacc[dt] *= alpha;
+  }
+  // O^T += V^T . P^T, operands read one k-step ahead of their MFMAs.
+  f16x8 vf[2];
+  vf[0] = v_frag(cur, 0, 0, 0, lane);
+#pragma unroll
+  for (int st = 0; st < 16; st++) {
+    if (st + 1 < 16) vf[(st + 1) & 1] = v_frag(cur, (st + 1) >> 2, ((st + 1) & 3) >> 1, (st + 1) & 1, lane);
+    oacc[st >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1], pf[st & 3], oacc[st >> 2], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const float* __restrict__ k_hs, const uint8_t* __restrict__ v_codes, const uint8_t* __restrict__ v_scales,
     const float* __restrict__ v_hs, int q_tokens, int64_t cache_tokens, int kv_tokens, float scale,
@@ -211,26 +245,21 @@ __global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
   const float c_k = scale * k_hs[h] * kLog2e;  // raw dot product -> log2 units
   const float s_gv = v_hs[h];
 
-  // Queries of this wave: two column tiles of 32; rows past q_tokens repeat the last row.
+  // Queries of this wave (one column tile of 32); rows past q_tokens repeat the last row.
   const int qbase = blockIdx.x * kABM + wave * kAQW;
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const int qi = min(qbase + 32 * qt + n, q_tokens - 1);
+  bf16x8 qf[8];
+  {
+    const int qi = min(qbase + n, q_tokens - 1);
     const __bf16* qrow = q + ((int64_t)h * q_tokens + qi) * kAD;
 #pragma unroll
-    for (int s = 0; s < 8; s++) qf[qt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+    for (int s = 0; s < 8; s++) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
   }
 
-  f32x16 oacc[2][4];
-#pragma unroll
-  for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) oacc[qt][dt] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  float m = -INFINITY, l = 0.0f;
 
   // Block 0 decoded into sm[0], block 1 prefetched into registers.
-  const int t_dec = threadIdx.x & 63, qd_dec = threadIdx.x >> 6;
+  const int t_dec = threadIdx.x & 63, qd_dec = threadIdx.x >> 6;  // token, NVFP4 block of head_dim
   const int nblk = (kv_tokens + kABN - 1) / kABN;
   RawKV raw;
   load_raw(raw, kc, ks, vc, vs, min(t_dec, kv_tokens - 1), qd_dec);
@@ -239,50 +268,7 @@ __global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
   __syncthreads();
 
   for (int blk = 0; blk < nblk; blk++) {
-    const AttnSmem& cur = sm[blk & 1];
-    // S^T = K . Q^T: sacc[qt][tau], lane (query n, half hh), element e ->
-    // token 32 tau + 8 (e / 4) + 4 hh + e % 4.
-    f32x16 sacc[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) sacc[qt][0] = sacc[qt][1] = f32x16{};
-    {
-      // K operands read two k-steps ahead of their MFMAs
-      bf16x8 kf[3];
-      kf[0] = k_frag(cur, 0, 0, lane);
-      kf[1] = k_frag(cur, 0, 1, lane);
-#pragma unroll
-      for (int st = 0; st < 16; st++) {
-        const int tau = st >> 3, s = st & 7;
-        if (st + 2 < 16) kf[(st + 2) % 3] = k_frag(cur, (st + 2) >> 3, (st + 2) & 7, lane);
-        sacc[0][tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st % 3], qf[0][s], sacc[0][tau], 0, 0, 0);
-        sacc[1][tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st % 3], qf[1][s], sacc[1][tau], 0, 0, 0);
-      }
-    }
-
-    const bool masked = blk + 1 == nblk && kv_tokens % kABN != 0;
-    const int valid = kv_tokens - blk * kABN;
-    f16x8 pf[2][4];
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-      const float alpha = softmax_tile(sacc[qt], c_k, masked, valid, hh, m[qt], l[qt], pf[qt]);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // the running max moved for some query
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) oacc[qt][dt] *= alpha;
-      }
-    }
-    // O^T += V^T . P^T: each V operand serves both query tiles; operands are
-    // read one k-step ahead of their MFMAs.
-    {
-      f16x8 vf[2];
-      vf[0] = v_frag(cur, 0, 0, 0, lane);
-#pragma unroll
-      for (int st = 0; st < 16; st++) {
-        const int dt = st >> 2, u = st & 3;
-        if (st + 1 < 16) vf[(st + 1) & 1] = v_frag(cur, (st + 1) >> 2, ((st + 1) & 3) >> 1, (st + 1) & 1, lane);
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1], pf[0][u], oacc[0][dt], 0, 0, 0);
-        oacc[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1], pf[1][u], oacc[1][dt], 0, 0, 0);
-      }
-    }
+    attn_block(sm[blk & 1], qf, oacc, m, l, c_k, kv_tokens - blk * kABN, lane);
 
     // Next block: decode into the other LDS buffer (its last readers finished
     // before the previous barrier), prefetch the one after.
@@ -294,18 +280,15 @@ __global__ __launch_bounds__(256, 1) void attn_nvfp4_kv_kernel(
   }
 
   // o = s_gV * O / l, l = this lane's partial sum + the other half's.
-#pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32);
-    const float inv = s_gv / lt;
-    const int qi = qbase + 32 * qt + n;
-    if (qi >= q_tokens) continue;
+  const float inv = s_gv / (l + __shfl_xor(l, 32));
+  const int qi = qbase + n;
+  if (qi < q_tokens) {
     __bf16* orow = out + ((int64_t)h * q_tokens + qi) * kAD;
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
       for (int eg = 0; eg < 4; eg++) {  // head-dim 32 dt + 8 eg + 4 hh + (0..3)
-        const f32x16& a = oacc[qt][dt];
+        const f32x16& a = oacc[dt];
         const bf16x2 p0 = {(__bf16)(a[4 * eg] * inv), (__bf16)(a[4 * eg + 1] * inv)};
         const bf16x2 p1 = {(__bf16)(a[4 * eg + 2] * inv), (__bf16)(a[4 * eg + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * eg + 4 * hh) =
@@ -322,7 +305,7 @@ hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint
                                hipStream_t stream) {
   if (q_tokens == 0) return hipSuccess;
   const dim3 grid((unsigned)((q_tokens + kABM - 1) / kABM), (unsigned)heads);
-  return launch_kernel(attn_nvfp4_kv_kernel, grid, dim3(256), 0, stream, (const __bf16*)q, k_codes, k_scales, k_hs,
+  return launch_kernel(attn_nvfp4_kv_kernel, grid, dim3(kAW * 64), 0, stream, (const __bf16*)q, k_codes, k_scales, k_hs,
                        v_codes, v_scales, v_hs, (int)q_tokens, cache_tokens, (int)kv_tokens, scale, (__bf16*)out);
 }
 
