@@ -247,12 +247,14 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     Tq = 4096
     qa = workloads.attention_queries(H, Tq, D).to(dev)
     oa = torch.empty_like(qa)
-    ms_a = time_calls(torch, lambda: nvfp4.kv_attention(qa, qk, qv, out=oa), 5, 2)
+    wsa = torch.empty(nvfp4.kv_attention_workspace_size(H, Tq, T, D), dtype=torch.uint8, device=dev)
+    ms_a = time_calls(torch, lambda: nvfp4.kv_attention(qa, qk, qv, out=oa, workspace=wsa), 5, 2)
     flop_a = 4.0 * H * Tq * T * D
     res["kv_attention"] = {"heads": H, "q_tokens": Tq, "kv_tokens": T, "head_dim": D, "ms": round(ms_a, 4),
+                           "workspace_bytes": wsa.numel(),
                            "TFLOP/s": round(flop_a / (ms_a * 1e-3) / 1e12, 1),
                            "frac_of_fp16_peak": round(flop_a / (ms_a * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
-    del qa, oa
+    del qa, oa, wsa
     ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}

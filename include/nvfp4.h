@@ -46,6 +46,7 @@
 #ifndef NVFP4_H_
 #define NVFP4_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -200,12 +201,26 @@ nvfp4_status_t kv_dequantize(const uint8_t *codes, const uint8_t *scales, const 
  *   parallel dequantization kernel for the attention) and the arXiv abstract
  *   (NVFP4 KV cache).  Requires head_dim == 128, 1 <= kv_tokens <=
  *   cache_tokens < 2^31, a finite softmax_scale; q_tokens == 0 is a no-op.
+ *   workspace: optional device memory (16-byte aligned, owned by the caller,
+ *   contents ignored and overwritten) of workspace_bytes bytes.  With at least
+ *   kv_attention_workspace_size() bytes the cache is split across more
+ *   workgroups when that balances the GPU better (fp32 partial results merged
+ *   by a second kernel); with less, or NULL, the split is limited to what fits
+ *   (none at 0).  Calls that share a workspace must not overlap.
  */
 nvfp4_status_t kv_attention(const void *q, int64_t heads, int64_t q_tokens, int64_t head_dim,
                             const uint8_t *k_codes, const uint8_t *k_scales, const float *k_head_scales,
                             const uint8_t *v_codes, const uint8_t *v_scales, const float *v_head_scales,
                             int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, void *out,
-                            void *stream);
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes at which kv_attention takes its preferred cache split for
+ * these sizes on the current device (0 if it would not split), written to
+ * *bytes.  Same shape rules as kv_attention (cache_tokens not needed).
+ */
+nvfp4_status_t kv_attention_workspace_size(int64_t heads, int64_t q_tokens, int64_t head_dim,
+                                           int64_t kv_tokens, size_t *bytes);
 
 #ifdef __cplusplus
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/nvfp4.h"
@@ -195,10 +196,21 @@ nvfp4_status_t kv_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                                         nvfp4::kDtypeBf16, (hipStream_t)stream));
 }
 
+nvfp4_status_t kv_attention_workspace_size(int64_t heads, int64_t q_tokens, int64_t head_dim, int64_t kv_tokens,
+                                           size_t* bytes) {
+  if (!bytes) return NVFP4_ERR_NULL;
+  if (head_dim != 128 || heads <= 0 || heads > 65535 || q_tokens < 0 || q_tokens >= (int64_t(1) << 31) ||
+      kv_tokens <= 0 || kv_tokens >= (int64_t(1) << 31) || (q_tokens > 0 && heads > kMaxElems / (q_tokens * head_dim)))
+    return NVFP4_ERR_SHAPE;
+  *bytes = (size_t)nvfp4::kv_attention_workspace_bytes(heads, q_tokens, kv_tokens);
+  return NVFP4_OK;
+}
+
 nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim, const uint8_t* k_codes,
                             const uint8_t* k_scales, const float* k_head_scales, const uint8_t* v_codes,
                             const uint8_t* v_scales, const float* v_head_scales, int64_t cache_tokens,
-                            int64_t kv_tokens, float softmax_scale, void* out, void* stream) {
+                            int64_t kv_tokens, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   if (head_dim != 128 || heads <= 0 || heads > 65535 || q_tokens < 0 || q_tokens >= (int64_t(1) << 31) ||
       kv_tokens <= 0 || kv_tokens > cache_tokens || cache_tokens >= (int64_t(1) << 31) ||
       heads > kMaxElems / (cache_tokens * head_dim) || (q_tokens > 0 && heads > kMaxElems / (q_tokens * head_dim)) ||
@@ -208,11 +220,13 @@ nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int6
       (q_tokens > 0 && (!q || !out)))
     return NVFP4_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
-      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(k_head_scales, 4) || !aligned(v_head_scales, 4))
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(k_head_scales, 4) || !aligned(v_head_scales, 4) ||
+      !aligned(workspace, 16))
     return NVFP4_ERR_ALIGN;
+  const int64_t ws = workspace ? (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX) : 0;
   return from_hip(nvfp4::launch_kv_attention(q, k_codes, k_scales, k_head_scales, v_codes, v_scales, v_head_scales,
-                                             heads, q_tokens, cache_tokens, kv_tokens, softmax_scale, out,
-                                             (hipStream_t)stream));
+                                             heads, q_tokens, cache_tokens, kv_tokens, softmax_scale, out, workspace,
+                                             ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -28,6 +28,13 @@
 // The tokens of an MFMA k-step are ordered to match the score layout, so P
 // goes from the softmax to the MFMA without any exchange.
 //
+// Load balance (flash-decoding split): when (query blocks x heads) would
+// leave CUs idle or a ragged last round, the cache is cut into `splits`
+// ranges of whole blocks, one workgroup per (query block, head, range); each
+// writes its unnormalised O, running max m and sum l in fp32 to a workspace
+// and a combine kernel merges the ranges:
+//   o = s_gV * sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r,  M = max_r m_r.
+//
 // LDS layouts (64 tokens x 256 B each, swizzled so that the decode writes,
 // the K operand reads and the transposing V reads are all bank-conflict
 // free):
@@ -232,9 +239,12 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     const float* __restrict__ k_hs, const uint8_t* __restrict__ v_codes, const uint8_t* __restrict__ v_scales,
     const float* __restrict__ v_hs, int q_tokens, int64_t cache_tokens, int kv_tokens, float scale,
-    __bf16* __restrict__ out) {
+    __bf16* __restrict__ out, int blocks_per_split, float* __restrict__ part_o, float2* __restrict__ part_ml) {
   __shared__ AttnSmem sm[2];
   const int h = blockIdx.y;
+  // this workgroup's cache blocks [blk0, blk1) (never empty: the host sizes the ranges)
+  const int blk0 = blockIdx.z * blocks_per_split;
+  const int blk1 = min((kv_tokens + kABN - 1) / kABN, blk0 + blocks_per_split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int64_t cache_row0 = (int64_t)h * cache_tokens;
@@ -258,30 +268,48 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   float m = -INFINITY, l = 0.0f;
 
-  // Block 0 decoded into sm[0], block 1 prefetched into registers.
+  // First block decoded into sm[0], the next prefetched into registers.
   const int t_dec = threadIdx.x & 63, qd_dec = threadIdx.x >> 6;  // token, NVFP4 block of head_dim
-  const int nblk = (kv_tokens + kABN - 1) / kABN;
   RawKV raw;
-  load_raw(raw, kc, ks, vc, vs, min(t_dec, kv_tokens - 1), qd_dec);
+  load_raw(raw, kc, ks, vc, vs, min(blk0 * kABN + t_dec, kv_tokens - 1), qd_dec);
   decode_to_lds(raw, sm[0], t_dec, qd_dec);
-  if (nblk > 1) load_raw(raw, kc, ks, vc, vs, min(kABN + t_dec, kv_tokens - 1), qd_dec);
+  if (blk0 + 1 < blk1) load_raw(raw, kc, ks, vc, vs, min((blk0 + 1) * kABN + t_dec, kv_tokens - 1), qd_dec);
   __syncthreads();
 
-  for (int blk = 0; blk < nblk; blk++) {
-    attn_block(sm[blk & 1], qf, oacc, m, l, c_k, kv_tokens - blk * kABN, lane);
+  for (int blk = blk0; blk < blk1; blk++) {
+    const int buf = (blk - blk0) & 1;
+    attn_block(sm[buf], qf, oacc, m, l, c_k, kv_tokens - blk * kABN, lane);
 
     // Next block: decode into the other LDS buffer (its last readers finished
     // before the previous barrier), prefetch the one after.
-    if (blk + 1 < nblk) {
-      decode_to_lds(raw, sm[(blk + 1) & 1], t_dec, qd_dec);
-      if (blk + 2 < nblk) load_raw(raw, kc, ks, vc, vs, min((blk + 2) * kABN + t_dec, kv_tokens - 1), qd_dec);
+    if (blk + 1 < blk1) {
+      decode_to_lds(raw, sm[buf ^ 1], t_dec, qd_dec);
+      if (blk + 2 < blk1) load_raw(raw, kc, ks, vc, vs, min((blk + 2) * kABN + t_dec, kv_tokens - 1), qd_dec);
     }
     __syncthreads();
   }
 
-  // o = s_gV * O / l, l = this lane's partial sum + the other half's.
-  const float inv = s_gv / (l + __shfl_xor(l, 32));
+  // l = this lane's partial sum + the other half's.
+  const float lt = l + __shfl_xor(l, 32);
   const int qi = qbase + n;
+  if (part_o) {  // one range of a split cache: unnormalised O, m, l for the combine
+    if (qi < q_tokens) {
+      const int64_t row = ((int64_t)blockIdx.z * gridDim.y + h) * q_tokens + qi;
+      float* prow = part_o + row * kAD;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int eg = 0; eg < 4; eg++) {
+          const f32x16& a = oacc[dt];
+          *reinterpret_cast<f32x4*>(prow + 32 * dt + 8 * eg + 4 * hh) =
+              f32x4{a[4 * eg], a[4 * eg + 1], a[4 * eg + 2], a[4 * eg + 3]};
+        }
+      if (hh == 0) part_ml[row] = make_float2(m, lt);
+    }
+    return;
+  }
+  // o = s_gV * O / l
+  const float inv = s_gv / lt;
   if (qi < q_tokens) {
     __bf16* orow = out + ((int64_t)h * q_tokens + qi) * kAD;
 #pragma unroll
@@ -297,16 +325,94 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
   }
 }
 
+// Merge the cache ranges of a split attention: 32 lanes per query, 4 head-dim
+// columns each.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           const float* __restrict__ v_hs, int splits, int heads,
+                                                           int q_tokens, __bf16* __restrict__ out) {
+  const int64_t rows = (int64_t)heads * q_tokens;
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  if (row >= rows) return;
+  const int c4 = (threadIdx.x & 31) * 4;
+  float mx = -INFINITY;
+  for (int r = 0; r < splits; r++) mx = fmaxf(mx, part_ml[r * rows + row].x);
+  float lsum = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < splits; r++) {
+    const float2 ml = part_ml[r * rows + row];
+    const float w = __builtin_amdgcn_exp2f(ml.x - mx);
+    lsum = __builtin_fmaf(w, ml.y, lsum);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + (r * rows + row) * kAD + c4);
+    acc += w * o;
+  }
+  const float inv = v_hs[row / q_tokens] / lsum;
+  const bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
+  const bf16x2 p1 = {(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(out + row * kAD + c4) = u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+}
+
+struct AttnSplit {
+  int splits;            // cache ranges (1: no split, no workspace)
+  int blocks_per_split;  // cache blocks per range
+};
+
+int64_t split_workspace_bytes(int64_t heads, int64_t q_tokens, int splits) {
+  return splits > 1 ? (int64_t)splits * heads * q_tokens * (kAD * 4 + 8) : 0;
+}
+
+// The number of cache ranges that minimises the modelled time, in units of one
+// workgroup's pass over one cache block: rounds of resident workgroups (one
+// per CU) x (blocks per range + a fixed start-up cost), plus the partial
+// results' HBM round trip in the combine.  Only splits whose workspace fits in
+// max_bytes are considered.
+AttnSplit choose_split(int64_t heads, int64_t q_tokens, int64_t kv_tokens, int64_t max_bytes) {
+  const int64_t wgs = (q_tokens + kABM - 1) / kABM * heads;
+  const int64_t nblk = (kv_tokens + kABN - 1) / kABN;
+  const int64_t cus = device_cu_count();
+  AttnSplit best{1, (int)nblk};
+  double best_cost = 0.0;
+  for (int sp = 1; sp <= 32; sp++) {
+    const int64_t bps = (nblk + sp - 1) / sp;
+    if ((nblk + bps - 1) / bps != sp || (sp > 1 && bps < 4)) continue;  // every range non-empty, >= 4 blocks
+    if (split_workspace_bytes(heads, q_tokens, sp) > max_bytes) continue;
+    const double rounds = (double)((wgs * sp + cus - 1) / cus);
+    double cost = rounds * (double)(bps + 3);
+    if (sp > 1) cost += 3.0 + (double)(split_workspace_bytes(heads, q_tokens, sp) + heads * q_tokens * kAD * 2) / 5.2e6;
+    if (sp == 1 || cost < best_cost) {
+      best_cost = cost;
+      best = AttnSplit{sp, (int)bps};
+    }
+  }
+  return best;
+}
+
 }  // namespace
+
+int64_t kv_attention_workspace_bytes(int64_t heads, int64_t q_tokens, int64_t kv_tokens) {
+  if (q_tokens == 0) return 0;
+  const AttnSplit sp = choose_split(heads, q_tokens, kv_tokens, INT64_MAX);
+  return split_workspace_bytes(heads, q_tokens, sp.splits);
+}
 
 hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint8_t* k_scales, const float* k_hs,
                                const uint8_t* v_codes, const uint8_t* v_scales, const float* v_hs, int64_t heads,
                                int64_t q_tokens, int64_t cache_tokens, int64_t kv_tokens, float scale, void* out,
-                               hipStream_t stream) {
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   if (q_tokens == 0) return hipSuccess;
-  const dim3 grid((unsigned)((q_tokens + kABM - 1) / kABM), (unsigned)heads);
-  return launch_kernel(attn_nvfp4_kv_kernel, grid, dim3(kAW * 64), 0, stream, (const __bf16*)q, k_codes, k_scales, k_hs,
-                       v_codes, v_scales, v_hs, (int)q_tokens, cache_tokens, (int)kv_tokens, scale, (__bf16*)out);
+  const AttnSplit sp = choose_split(heads, q_tokens, kv_tokens, workspace ? workspace_bytes : 0);
+  const dim3 grid((unsigned)((q_tokens + kABM - 1) / kABM), (unsigned)heads, (unsigned)sp.splits);
+  float* part_o = sp.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  float2* part_ml = sp.splits > 1 ? reinterpret_cast<float2*>(part_o + (int64_t)sp.splits * heads * q_tokens * kAD)
+                                  : nullptr;
+  hipError_t e = launch_kernel(attn_nvfp4_kv_kernel, grid, dim3(kAW * 64), 0, stream, (const __bf16*)q, k_codes,
+                               k_scales, k_hs, v_codes, v_scales, v_hs, (int)q_tokens, cache_tokens, (int)kv_tokens,
+                               scale, (__bf16*)out, sp.blocks_per_split, part_o, part_ml);
+  if (e != hipSuccess || sp.splits == 1) return e;
+  const int64_t threads = heads * q_tokens * 32;
+  return launch_kernel(attn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)part_o, (const float2*)part_ml, v_hs, sp.splits, (int)heads, (int)q_tokens,
+                       (__bf16*)out);
 }
 
 }  // namespace nvfp4

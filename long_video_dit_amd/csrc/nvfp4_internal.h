@@ -50,7 +50,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
 hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint8_t* k_scales, const float* k_hs,
                                const uint8_t* v_codes, const uint8_t* v_scales, const float* v_hs, int64_t heads,
                                int64_t q_tokens, int64_t cache_tokens, int64_t kv_tokens, float scale, void* out,
-                               hipStream_t stream);
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream);
+// Workspace bytes at which launch_kv_attention takes its preferred cache split
+// on the current device (0: no split).
+int64_t kv_attention_workspace_bytes(int64_t heads, int64_t q_tokens, int64_t kv_tokens);
 
 // W4A4 GEMM launcher (nvfp4_gemm.hip).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,

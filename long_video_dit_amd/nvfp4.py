@@ -29,7 +29,9 @@ SIGNATURES = {
     "kv_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kv_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P]),
-    "kv_attention": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P]),
+    "kv_attention": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
+                          ctypes.c_size_t, _P]),
+    "kv_attention_workspace_size": (_I, [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
 }
 
 _lib = None
@@ -186,9 +188,18 @@ def kv_dequantize(codes, scales, head_scales, out=None):
     return y
 
 
-def kv_attention(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None):
+def kv_attention_workspace_size(heads, q_tokens, kv_tokens, head_dim=128):
+    """Workspace bytes at which kv_attention takes its preferred cache split on the current device."""
+    n = ctypes.c_size_t(0)
+    _call("kv_attention_workspace_size", heads, q_tokens, head_dim, kv_tokens, ctypes.byref(n))
+    return n.value
+
+
+def kv_attention(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None, workspace=None):
     """Softmax attention of q bf16 [H, Tq, D] over the first kv_tokens rows of the NVFP4 caches
-    k_cache, v_cache = (codes [H, T, D/2], scales [H, T, D/16], head_scales [H]); bf16 [H, Tq, D]."""
+    k_cache, v_cache = (codes [H, T, D/2], scales [H, T, D/16], head_scales [H]); bf16 [H, Tq, D].
+    workspace: optional uint8 device tensor for the split-cache partial results (allocated here at
+    the preferred size when None; an empty tensor turns the split off)."""
     _need_cuda(q, *k_cache, *v_cache)
     H, Tq, D = q.shape
     kc, ks, kh = k_cache
@@ -197,6 +208,12 @@ def kv_attention(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None):
     kv_tokens = T if kv_tokens is None else kv_tokens
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        with torch.cuda.device(q.device):
+            nbytes = kv_attention_workspace_size(H, Tq, kv_tokens, D)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _need_cuda(workspace)
     _call("kv_attention", _ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kh), _ptr(vc), _ptr(vs), _ptr(vh), T, kv_tokens,
-          float(scale), _ptr(o), _stream(q.device))
+          float(scale), _ptr(o), _ptr(workspace) if workspace.numel() else None, workspace.numel(),
+          _stream(q.device))
     return o

@@ -100,7 +100,7 @@ def test_validation_errors_launch_nothing():
     assert lib.kv_quantize_append(None, 4, 16, 128, buf, buf, buf, 64, 0, None) == nv.ERR_NULL
     assert lib.kv_quantize_append(buf, 4, 16, 128, buf, odd, buf, 64, 0, None) == nv.ERR_ALIGN
     assert lib.kv_quantize_append(buf, 4, 0, 128, buf, buf, buf, 64, 64, None) == nv.OK  # empty append
-    kva = lambda *a: lib.kv_attention(*a)
+    kva = lambda *a: lib.kv_attention(*a[:-1], None, 0, a[-1])
     assert kva(buf, 2, 8, 64, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_SHAPE  # head_dim 128
     assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 33, 0.1, buf, None) == nv.ERR_SHAPE  # > cache
     assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 0, 0.1, buf, None) == nv.ERR_SHAPE
@@ -108,8 +108,38 @@ def test_validation_errors_launch_nothing():
     assert kva(buf, 2, 8, 128, buf, buf, None, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_NULL
     assert kva(None, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_NULL
     assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, odd, None) == nv.ERR_ALIGN
+    assert lib.kv_attention(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, odd, 64,
+                            None) == nv.ERR_ALIGN  # workspace
+    n = ctypes.c_size_t(7)
+    assert lib.kv_attention_workspace_size(2, 8, 64, 32, ctypes.byref(n)) == nv.ERR_SHAPE
+    assert lib.kv_attention_workspace_size(2, 8, 128, 0, ctypes.byref(n)) == nv.ERR_SHAPE
+    assert lib.kv_attention_workspace_size(0, 8, 128, 32, ctypes.byref(n)) == nv.ERR_SHAPE
+    assert lib.kv_attention_workspace_size(2, 8, 128, 32, None) == nv.ERR_NULL
+    assert n.value == 7
     assert lib.kv_dequantize(buf, buf, buf, 4, -1, 128, buf, None) == nv.ERR_SHAPE
     assert lib.kv_dequantize(buf, buf, buf, 4, 16, 128, odd, None) == nv.ERR_ALIGN
+
+
+def test_attention_split_choice():
+    """Host logic of the split-cache attention (a GPU-less host counts 256 CUs,
+    as an MI355X has): the workspace it asks for is a whole number of
+    per-range partial buffers (fp32 O plus m and l per query, 520 B), none
+    when the grid already fills whole rounds of the CUs or the cache is too
+    short to cut, and a split when few workgroups would leave CUs idle."""
+    from long_video_dit_amd import nvfp4 as nv
+    if nv.lib().nvfp4_abi_version() < 1:
+        pytest.skip("library too old")
+    ws = nv.kv_attention_workspace_size
+    per = lambda H, Tq: H * Tq * 520
+    assert ws(32, 2048, 65536) == 0          # 8 query blocks x 32 heads = one full round
+    assert ws(24, 4096, 200) == 0            # 4 cache blocks: nothing to cut
+    assert ws(24, 0, 65536) == 0
+    b = ws(24, 256, 65536)                   # 24 workgroups for 256 CUs
+    assert b > 0 and b % per(24, 256) == 0 and b // per(24, 256) >= 8
+    b = ws(24, 4096, 65536)                  # 384 workgroups: 1.5 rounds unsplit
+    assert b > 0 and b % per(24, 4096) == 0
+    b = ws(1, 1, 1 << 20)                    # one query, a long cache: split at most 32 ways
+    assert 0 < b // per(1, 1) <= 32
 
 
 def test_gemm_fast_path_leaves_m0_to_the_lds_copies():

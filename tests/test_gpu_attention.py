@@ -26,7 +26,9 @@ def _nv():
     return nvfp4
 
 
-def _run(H, Tq, Tc, T, seed, qscale=1.0, scale=None, q_idx=None):
+def _run(H, Tq, Tc, T, seed, qscale=1.0, scale=None, q_idx=None, workspaces=(None,)):
+    """workspaces: kv_attention's workspace per run (None: the preferred split;
+    an int: a workspace of that many bytes, 0 turning the split off)."""
     nv = _nv()
     D = 128
     k, v = workloads.kv_cache(H, Tc, D, sinks=min(4, Tc))
@@ -34,7 +36,10 @@ def _run(H, Tq, Tc, T, seed, qscale=1.0, scale=None, q_idx=None):
     q = (torch.randn(H, Tq, D, generator=g) * qscale).to(torch.bfloat16)
     scale = D ** -0.5 if scale is None else scale
     kq, vq = nv.kv_quantize(k.to(dev())), nv.kv_quantize(v.to(dev()))
-    o = nv.kv_attention(q.to(dev()), kq, vq, T, scale)
+    outs = []
+    for w in workspaces:
+        wt = None if w is None else torch.empty(w, dtype=torch.uint8, device=dev())
+        outs.append(nv.kv_attention(q.to(dev()), kq, vq, T, scale, workspace=wt))
     torch.cuda.synchronize()
     ok, ov = oracle.kv_quantize(workloads.bf16_bits(k)), oracle.kv_quantize(workloads.bf16_bits(v))
     for g_, o_ in zip(list(kq) + list(vq), list(ok) + list(ov)):  # the caches fed to the oracle are its own
@@ -42,16 +47,17 @@ def _run(H, Tq, Tc, T, seed, qscale=1.0, scale=None, q_idx=None):
     ref, wabs = oracle.kv_attention(workloads.bf16_bits(q), ok, ov, T, scale, q_idx=q_idx)
     vf = np.stack([oracle.dequantize(ov[0][h, :T], ov[1][h, :T], ov[2][h], "f32") for h in range(H)])
     vmax = np.abs(vf).max(axis=1)[:, None, :]
-    got = c_to_f64(o)
-    if q_idx is not None:
-        got = got[:, q_idx]
-    err = np.abs(got - ref)
-    tol = np.maximum(half_ulp_bf16(ref), half_ulp_bf16(got)) + 2.0 ** -9 * wabs + 2.0 ** -25 * T * vmax
-    ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
-    worst = float(ratio.max())
-    log("attention", H, Tq, Tc, T, "worst err/tol %.3g, max err %.3g" % (worst, err.max()))
-    assert worst <= 1.0, "error exceeds the bound: worst err/tol %.3g at %s" % (
-        worst, np.unravel_index(int(ratio.argmax()), err.shape))
+    for w, o in zip(workspaces, outs):
+        got = c_to_f64(o)
+        if q_idx is not None:
+            got = got[:, q_idx]
+        err = np.abs(got - ref)
+        tol = np.maximum(half_ulp_bf16(ref), half_ulp_bf16(got)) + 2.0 ** -9 * wabs + 2.0 ** -25 * T * vmax
+        ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+        worst = float(ratio.max())
+        log("attention", H, Tq, Tc, T, "workspace", w, "worst err/tol %.3g, max err %.3g" % (worst, err.max()))
+        assert worst <= 1.0, "workspace %s: error exceeds the bound: worst err/tol %.3g at %s" % (
+            w, worst, np.unravel_index(int(ratio.argmax()), err.shape))
 
 
 @pytest.mark.parametrize("H,Tq,Tc,T", [(2, 100, 200, 150), (1, 1, 64, 1), (3, 300, 4096, 4096), (2, 257, 1000, 999),
@@ -68,3 +74,19 @@ def test_attention_peaked_softmax():
 def test_attention_full_cache_sampled_queries():
     """The 24-head 65,536-token cache, 1,024 queries per head; sampled query rows."""
     _run(24, 1024, 65536, 65536, seed=11, q_idx=np.array([0, 1, 255, 256, 511, 777, 1023]))
+
+
+def test_attention_split_cache_modes():
+    """The split-cache path against the same oracle: the preferred split (20
+    ranges of 4 blocks, the last one ragged, for 6 workgroups over 79 cache
+    blocks), a workspace that fits two ranges, and none (one pass)."""
+    H, Tq = 3, 300
+    per_range = H * Tq * 520
+    assert _nv().kv_attention_workspace_size(H, Tq, 4999) > 2 * per_range
+    _run(H, Tq, 5000, 4999, seed=21, workspaces=(None, 2 * per_range + 100, 0))
+
+
+def test_attention_split_one_query():
+    """One query per head over a long cache: most workgroups hold one range of
+    a single query's cache."""
+    _run(4, 1, 20000, 19990, seed=22, qscale=3.0, workspaces=(None, 0))
