@@ -159,6 +159,15 @@ def quantize(x, s_g=None):
     return codes, scales, np.float32(s_g)
 
 
+def quantize_transposed(x, s_g=None):
+    """x [rows, cols] quantized along its rows: the NVFP4 form of x.T, i.e. blocks of 16
+    consecutive rows of one column -> (codes [cols, rows/2], scales [cols, rows/16], s_g).
+    By definition this is quantize() of the transposed matrix (the pages put NVFP4 on the
+    training GEMMs too: landx.limxdynamics.com, sections on NVFP4 and on the training stage;
+    d9249.github.io review, "Core idea / structure / operation"); s_g is the same as for x."""
+    return quantize(np.ascontiguousarray(np.asarray(x).T), s_g)
+
+
 def dequantize(codes, scales, s_g, out="bf16"):
     """-> bf16 bit patterns (uint16) or float32 [rows, k]."""
     codes = np.ascontiguousarray(codes, np.uint8)
