@@ -211,7 +211,8 @@ def main():
 
 
 def secondary(torch, nvfp4, workloads, dev, a3, aq3):
-    """HBM throughput of the quantizer and the NVFP4 KV-cache round trip."""
+    """HBM throughput of the quantizer and the NVFP4 KV-cache round trip, the attention over
+    the packed cache, and the backward operands and GEMMs of the FFN up-projection."""
     res = {}
     # activation quantize of the FFN down-projection input (bf16 [16384, 14336], 470 MB)
     a4 = workloads.activations(4).to(dev)
@@ -248,7 +249,9 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     qa = workloads.attention_queries(H, Tq, D).to(dev)
     oa = torch.empty_like(qa)
     wsa = torch.empty(nvfp4.kv_attention_workspace_size(H, Tq, T, D), dtype=torch.uint8, device=dev)
-    ms_a = time_calls(torch, lambda: nvfp4.kv_attention(qa, qk, qv, out=oa, workspace=wsa), 5, 2)
+    attn = lambda: nvfp4.kv_attention(qa, qk, qv, out=oa, workspace=wsa)
+    settle(torch, attn)
+    ms_a = time_calls(torch, attn, 10, 2)
     flop_a = 4.0 * H * Tq * T * D
     res["kv_attention"] = {"heads": H, "q_tokens": Tq, "kv_tokens": T, "head_dim": D, "ms": round(ms_a, 4),
                            "workspace_bytes": wsa.numel(),
@@ -259,6 +262,30 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}
     res["kv_dequantize"] = {"ms": round(ms_d, 4), "GB/s": round(k.numel() * B_DEQUANT / (ms_d * 1e-3) / 1e9, 1)}
+    # backward of the FFN up-projection: dY [16384, 14336] quantized along its rows (the wgrad
+    # operand), dX = dY W (contracting 14336) and dW = dY^T A (contracting 16384)
+    del k, v, qk, qv, ok, ov
+    w3, dy = workloads.weights(3).to(dev), workloads.output_grads(3).to(dev)
+    dyq, wtq, dytq, atq = nvfp4.quantize(dy), nvfp4.quantize_transposed(w3), nvfp4.quantize_transposed(dy), \
+        nvfp4.quantize_transposed(a3)
+    qt = lambda: nvfp4.quantize_transposed(dy, out=dytq[:2], s_g_out=dytq[2])
+    settle(torch, qt)
+    ms_t = time_calls(torch, qt, 10, 2)
+    dx = torch.empty(dy.shape[0], w3.shape[1], dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(w3.shape, dtype=torch.bfloat16, device=dev)
+    dgrad = lambda: nvfp4.gemm(dyq, wtq, out=dx)
+    wgrad = lambda: nvfp4.gemm(dytq, atq, out=dw)
+    settle(torch, dgrad)
+    ms_dx = time_calls(torch, dgrad, 10, 2)
+    ms_dw = time_calls(torch, wgrad, 10, 2)
+    M3, N3, K3 = dy.shape[0], dy.shape[1], w3.shape[1]
+    fl = 2.0 * M3 * N3 * K3
+    res["backward_ffn_up"] = {
+        "quantize_transposed_dY": {"shape": [M3, N3], "ms": round(ms_t, 4),
+                                   "GB/s": round(dy.numel() * (B_AMAX + B_ENCODE) / (ms_t * 1e-3) / 1e9, 1)},
+        "dgrad_dX_16384x3072x14336": {"ms": round(ms_dx, 4), "TFLOP/s": round(fl / (ms_dx * 1e-3) / 1e12, 1)},
+        "wgrad_dW_14336x3072x16384": {"ms": round(ms_dw, 4), "TFLOP/s": round(fl / (ms_dw * 1e-3) / 1e12, 1)}}
+    del w3, dy, dyq, wtq, dytq, atq, dx, dw
     res["hbm_peak_GB/s"] = HBM_PEAK_GBS
     log("secondary", json.dumps(res))
     return res

@@ -107,6 +107,31 @@ nvfp4_status_t nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t k,
                               uint8_t *scales, float *s_g, int flags, void *stream);
 
 /*
+ * Quantize x [rows][cols] (dtype F32 or BF16, row-major) along its rows:
+ * the NVFP4 form of x^T, with blocks of 16 consecutive rows of one column.
+ *   codes_t  [cols][rows/2]  u8 out      scales_t [cols][rows/16] u8 out
+ *   s_g      [1] fp32: out with NVFP4_SCALE_COMPUTE (the same value as for x
+ *            itself: the amax does not depend on the layout), in with
+ *            NVFP4_SCALE_GIVEN
+ * Bit-identical to nvfp4_quantize of a transposed copy of x, without
+ * writing that copy.  These are the operands of the backward GEMMs of a
+ * linear Y = X W^T in nn.Linear layout (nvfp4_gemm contracts over the
+ * contiguous axis): dX = dY W takes W quantized along its rows (this call on
+ * W) against dY quantized row-wise; dW = dY^T X takes dY and X quantized
+ * along their rows (this call on both).  The landx.limxdynamics.com article
+ * (sections on NVFP4 and on the training stage) and the d9249.github.io
+ * review (section "Core idea / structure / operation") put NVFP4 on the
+ * training GEMMs too; the pages do not define the recipe, so the rounding is
+ * the same single RNE as everywhere else (no stochastic rounding, no
+ * Hadamard transform).  cols == 0 is allowed (COMPUTE then writes s_g = 0);
+ * the codes buffer serves as scratch for the amax partials.  Requires
+ * rows > 0, rows % 16 == 0, rows * cols < 2^40.
+ */
+nvfp4_status_t nvfp4_quantize_transposed(const void *x, int dtype, int64_t rows, int64_t cols,
+                                         uint8_t *codes_t, uint8_t *scales_t, float *s_g, int flags,
+                                         void *stream);
+
+/*
  * Dequantize: y[r][i] = RN_ydtype(val(code) * val(scale) * s_g), y [rows][k]
  * of dtype F32 or BF16 (one rounding of the exact product).  Same shape
  * rules as nvfp4_quantize.  Per the d9249.github.io review (dequantization

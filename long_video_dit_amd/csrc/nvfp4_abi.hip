@@ -92,6 +92,23 @@ nvfp4_status_t nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t k,
   return from_hip(nvfp4::launch_encode(x, dtype, units, 1, s_g, reinterpret_cast<uint32_t*>(codes), scales, s));
 }
 
+nvfp4_status_t nvfp4_quantize_transposed(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes_t,
+                                         uint8_t* scales_t, float* s_g, int flags, void* stream) {
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  nvfp4_status_t st = check_matrix(cols, rows, true);  // x^T is [cols][rows], blocks along rows
+  if (st != NVFP4_OK) return st;
+  if (!s_g || (cols > 0 && (!x || !codes_t || !scales_t))) return NVFP4_ERR_NULL;
+  if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes_t, 16) || !aligned(scales_t, 4)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t units = rows * cols / 8;
+  if (flags == NVFP4_SCALE_COMPUTE) {
+    st = from_hip(nvfp4::launch_global_scale(x, dtype, units, 1, reinterpret_cast<uint32_t*>(codes_t), units, s_g, s));
+    if (st != NVFP4_OK) return st;
+  }
+  return from_hip(nvfp4::launch_encode_t(x, dtype, rows, cols, s_g, reinterpret_cast<uint32_t*>(codes_t), scales_t, s));
+}
+
 nvfp4_status_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t rows,
                                 int64_t k, void* y, int y_dtype, void* stream) {
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;

@@ -43,6 +43,9 @@ hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, flo
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
                          uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride = -1,
                          int64_t out_offset = 0);
+// Encode pass along rows: x [rows][cols] -> NVFP4 of x^T (rows % 16 == 0).
+hipError_t launch_encode_t(const void* x, int dtype, int64_t rows, int64_t cols, const float* s_g, uint32_t* codes,
+                           uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
                           int groups, void* y, int y_dtype, hipStream_t stream);
 

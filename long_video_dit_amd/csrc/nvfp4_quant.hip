@@ -11,6 +11,7 @@
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
 //   amax_slot_kernel     standalone s_g: atomic max into the s_g slot itself
 //   encode_kernel        pass 2: scale byte per 16, 8 codes per lane
+//   encode_t_kernel      pass 2 along the other axis: NVFP4 of x^T
 //   dequant_kernel       codes + scales -> bf16 / fp32, 8 outputs per lane
 //
 // The amax partials live in the caller's codes buffer (it is at least 4 B
@@ -238,6 +239,85 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
   }
 }
 
+// ---- transposed encode ---------------------------------------------------
+//
+// x [rows][cols] -> the NVFP4 form of x^T: codes [cols][rows / 2], scales
+// [cols][rows / 16], blocks of 16 consecutive rows of one column (the layout
+// the backward GEMMs contract over: dgrad over the output features of W,
+// wgrad over tokens).  One workgroup per tile of 256 rows x 64 columns; lane
+// (c4 = lane % 16, rb = 4 wave + lane / 16) owns columns 4 c4 .. 4 c4 + 3 and
+// rows 16 rb .. 16 rb + 15 of the tile, i.e. four whole blocks, so the block
+// maximum needs no lane exchange.  Loads: the 16 lanes of one rb read one
+// contiguous row segment (128 B of bf16); stores: per column the tile's four
+// waves write its 128 code bytes contiguously.  Same rounding helpers as the
+// row-wise pass, so the result is bit-identical to quantizing x^T.
+constexpr int kTR = 256, kTC = 64;
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* __restrict__ p, float (&f)[4]);
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* __restrict__ p, float (&f)[4]) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4<float>(const float* __restrict__ p, float (&f)[4]) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  f[0] = v.x;
+  f[1] = v.y;
+  f[2] = v.z;
+  f[3] = v.w;
+}
+__device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(kThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                            const float* __restrict__ s_g,
+                                                            uint32_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const EncodeConsts c = make_encode_consts(s_g[0]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tiles_c = (cols + kTC - 1) / kTC;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTR + 16 * (4 * wave + (lane >> 4));
+  const int64_t col0 = (int64_t)(blockIdx.x % tiles_c) * kTC + 4 * (lane & 15);
+  if (r0 >= rows || col0 >= cols) return;  // rows % 16 == 0: a block is wholly in or out
+  float f[4][16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const T* row = x + (r0 + i) * cols + col0;
+    float v[4];
+    if (kVec) {
+      load4<T>(row, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] = col0 + j < cols ? load1(row + j) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) f[j][i] = v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (col0 + j >= cols) break;
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
+    const uint32_t sb = encode_scale(am, c);
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      lo[i] = f[j][i];
+      hi[i] = f[j][8 + i];
+    }
+    const int64_t col = col0 + j;
+    *reinterpret_cast<u32x2*>(codes + col * (rows / 8) + r0 / 8) = u32x2{encode8(lo, sb, c), encode8(hi, sb, c)};
+    scales[col * (rows / 16) + r0 / 16] = (uint8_t)sb;
+  }
+}
+
 // ---- launchers ----------------------------------------------------------
 
 static int grid_blocks(int64_t work_items, int per_thread, int max_blocks) {
@@ -298,6 +378,23 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
                          codes, scales, out_group_stride, out_offset);
   return launch_kernel(encode_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, units_per_group,
                        s_g, codes, scales, out_group_stride, out_offset);
+}
+
+hipError_t launch_encode_t(const void* x, int dtype, int64_t rows, int64_t cols, const float* s_g, uint32_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t tiles = (rows + kTR - 1) / kTR * ((cols + kTC - 1) / kTC);
+  const dim3 grid((unsigned)tiles);
+  const bool vec = cols % 4 == 0;
+  if (dtype == kDtypeF32)
+    return vec ? launch_kernel(encode_t_kernel<float, true>, grid, dim3(kThreads), 0, stream, (const float*)x, rows,
+                               cols, s_g, codes, scales)
+               : launch_kernel(encode_t_kernel<float, false>, grid, dim3(kThreads), 0, stream, (const float*)x, rows,
+                               cols, s_g, codes, scales);
+  return vec ? launch_kernel(encode_t_kernel<uint16_t, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x,
+                             rows, cols, s_g, codes, scales)
+             : launch_kernel(encode_t_kernel<uint16_t, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x,
+                             rows, cols, s_g, codes, scales);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,

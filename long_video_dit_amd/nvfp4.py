@@ -23,6 +23,7 @@ SIGNATURES = {
     "nvfp4_status_string": (ctypes.c_char_p, [_I]),
     "nvfp4_global_scale": (_I, [_P, _I, _I64, _I64, _P, _P]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P]),
+    "nvfp4_quantize_transposed": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm_fused_act": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _P]),
@@ -103,6 +104,25 @@ def quantize(x, s_g=None, out=None, s_g_out=None):
     if s_g is None:
         s_g = torch.empty(1, dtype=torch.float32, device=x.device) if s_g_out is None else s_g_out
     _call("nvfp4_quantize", _ptr(x), _dt(x), rows, k, _ptr(codes), _ptr(scales), _ptr(s_g), flags,
+          _stream(x.device))
+    return codes, scales, s_g
+
+
+def quantize_transposed(x, s_g=None, out=None, s_g_out=None):
+    """x [rows, cols] (float32/bfloat16, device) quantized along its rows: the NVFP4 form of x.T,
+    (codes u8 [cols, rows/2], scales u8 [cols, rows/16], s_g f32 [1]), without a transposed copy.
+    s_g, out and s_g_out as in quantize."""
+    _need_cuda(x)
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty(cols, rows // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(cols, rows // 16, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    flags = SCALE_COMPUTE if s_g is None else SCALE_GIVEN
+    if s_g is None:
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device) if s_g_out is None else s_g_out
+    _call("nvfp4_quantize_transposed", _ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(s_g), flags,
           _stream(x.device))
     return codes, scales, s_g
 

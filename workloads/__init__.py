@@ -20,6 +20,9 @@ torch.Generator seeded 1000*cfg + t, t = 0 activations/K, 1 weights/V,
   5  K, V bf16 [24, 65536, 128] ~ N(0, 1), tokens 0..3 of every head x8
      (attention-sink tokens); queries of a new chunk attending that cache
      bf16 [24, 4096, 128] ~ N(0, 1) (t = 2)
+  backward of a linear (configs 2-4): the output gradient dY bf16 [M, N] =
+     2^-12 * s_m * N(0, 1), s_m = exp(0.5 z_m) per token m (t = 3, z: t = 4);
+     with A and W of the config it feeds dX = dY W and dW = dY^T A
 Sizes can be overridden (same recipe) for small parity cases.
 """
 import torch
@@ -70,6 +73,16 @@ def weights(cfg, N=None, K=None):
         return w
     std = {2: 0.02, 3: 0.02, 4: 0.01}[cfg]
     return (w * std).to(torch.bfloat16)
+
+
+def output_grads(cfg, M=None, N=None):
+    """Output gradient dY [M, N] of the linear of config cfg (CPU tensor, bf16)."""
+    c = CONFIGS[cfg]
+    M = c["M"] if M is None else M
+    N = c["N"] if N is None else N
+    g = torch.randn(M, N, generator=generator(cfg, 3), dtype=torch.float32)
+    z = torch.randn(M, generator=generator(cfg, 4), dtype=torch.float32)
+    return (g * (2.0 ** -12) * torch.exp(0.5 * z)[:, None]).to(torch.bfloat16)
 
 
 def kv_cache(H=None, T=None, D=None, sinks=4):
