@@ -248,8 +248,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
 // (c4 = lane % 16, rb = 4 wave + lane / 16) owns columns 4 c4 .. 4 c4 + 3 and
 // rows 16 rb .. 16 rb + 15 of the tile, i.e. four whole blocks, so the block
 // maximum needs no lane exchange.  Loads: the 16 lanes of one rb read one
-// contiguous row segment (128 B of bf16); stores: per column the tile's four
-// waves write its 128 code bytes contiguously.  Same rounding helpers as the
+// contiguous row segment (128 B of bf16).  Codes and scale bytes are staged
+// in LDS per tile and stored column by column, 16 lanes x 8 B = one 128-byte
+// line of codes per column and 16 scale bytes per column, instead of 32-byte
+// pieces of 16 columns per instruction.  Same rounding helpers as the
 // row-wise pass, so the result is bit-identical to quantizing x^T.
 constexpr int kTR = 256, kTC = 64;
 
@@ -279,42 +281,68 @@ __global__ __launch_bounds__(kThreads) void encode_t_kernel(const T* __restrict_
                                                             const float* __restrict__ s_g,
                                                             uint32_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
+  // Staging: codes [64 columns][32 words + 2 pad], scales [64 columns][16 B].
+  __shared__ uint32_t sc[kTC][34];
+  __shared__ uint32_t ss[kTC][4];
   const EncodeConsts c = make_encode_consts(s_g[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tiles_c = (cols + kTC - 1) / kTC;
-  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTR + 16 * (4 * wave + (lane >> 4));
-  const int64_t col0 = (int64_t)(blockIdx.x % tiles_c) * kTC + 4 * (lane & 15);
-  if (r0 >= rows || col0 >= cols) return;  // rows % 16 == 0: a block is wholly in or out
-  float f[4][16];
+  const int64_t tr0 = (int64_t)(blockIdx.x / tiles_c) * kTR, tc0 = (int64_t)(blockIdx.x % tiles_c) * kTC;
+  const int rb = 4 * wave + (lane >> 4), c4 = lane & 15;
+  const int64_t r0 = tr0 + 16 * rb, col0 = tc0 + 4 * c4;
+  if (r0 < rows && col0 < cols) {  // rows % 16 == 0: a block is wholly in or out
+    float f[4][16];
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const T* row = x + (r0 + i) * cols + col0;
-    float v[4];
-    if (kVec) {
-      load4<T>(row, v);
-    } else {
+    for (int i = 0; i < 16; i++) {
+      const T* row = x + (r0 + i) * cols + col0;
+      float v[4];
+      if (kVec) {
+        load4<T>(row, v);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; j++) v[j] = col0 + j < cols ? load1(row + j) : 0.0f;
+        for (int j = 0; j < 4; j++) v[j] = col0 + j < cols ? load1(row + j) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) f[j][i] = v[j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; j++) f[j][i] = v[j];
+    for (int j = 0; j < 4; j++) {
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
+      const uint32_t sb = encode_scale(am, c);
+      float lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        lo[i] = f[j][i];
+        hi[i] = f[j][8 + i];
+      }
+      *reinterpret_cast<u32x2*>(&sc[4 * c4 + j][2 * rb]) = u32x2{encode8(lo, sb, c), encode8(hi, sb, c)};
+      reinterpret_cast<uint8_t*>(ss[4 * c4 + j])[rb] = (uint8_t)sb;
+    }
   }
+  __syncthreads();
+  // Codes: 16 lanes per column, lane p stores rows 16 p .. 16 p + 15 (8 B).
+  const int64_t words_per_col = rows / 8;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (col0 + j >= cols) break;
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
-    const uint32_t sb = encode_scale(am, c);
-    float lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      lo[i] = f[j][i];
-      hi[i] = f[j][8 + i];
+  for (int it = 0; it < kTC * 16 / kThreads; it++) {
+    const int idx = it * kThreads + threadIdx.x, cl = idx >> 4, p = idx & 15;
+    if (tc0 + cl < cols && tr0 + 16 * p < rows)
+      *reinterpret_cast<u32x2*>(codes + (tc0 + cl) * words_per_col + tr0 / 8 + 2 * p) =
+          *reinterpret_cast<const u32x2*>(&sc[cl][2 * p]);
+  }
+  // Scale bytes: 4 lanes per column, 4 bytes each when aligned.
+  {
+    const int cl = threadIdx.x >> 2, p = threadIdx.x & 3;
+    if (tc0 + cl < cols) {
+      uint8_t* dst = scales + (tc0 + cl) * (rows / 16) + tr0 / 16 + 4 * p;
+      if (rows % 64 == 0 && tr0 + 64 * (p + 1) <= rows) {
+        *reinterpret_cast<uint32_t*>(dst) = ss[cl][p];
+      } else {
+        for (int b = 0; b < 4; b++)
+          if (tr0 + 16 * (4 * p + b) < rows) dst[b] = reinterpret_cast<const uint8_t*>(ss[cl])[4 * p + b];
+      }
     }
-    const int64_t col = col0 + j;
-    *reinterpret_cast<u32x2*>(codes + col * (rows / 8) + r0 / 8) = u32x2{encode8(lo, sb, c), encode8(hi, sb, c)};
-    scales[col * (rows / 16) + r0 / 16] = (uint8_t)sb;
   }
 }
 
