@@ -372,6 +372,65 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
                           "oracle_roundtrip_ms_est": round(o_ms, 1), "oracle_sample": "1 head of K",
                           "oracle_threads": oracle.num_threads()}
     log("config 5", json.dumps(res[c["workload"]]))
+    # attention of a new 4096-query chunk over the packed config-5 cache
+    qa_cpu = workloads.attention_queries(H, 4096, D)
+    qa = qa_cpu.to(dev)
+    Tq = qa.shape[1]
+    oa = torch.empty_like(qa)
+    wsa = torch.empty(nvfp4.kv_attention_workspace_size(H, Tq, T, D), dtype=torch.uint8, device=dev)
+    attn = lambda: nvfp4.kv_attention(qa, qk, qv, out=oa, workspace=wsa)
+    settle(torch, attn)
+    a_ms = time_calls(torch, attn, steps, warmup)
+    flop_a = 4.0 * H * Tq * T * D
+    oks = oracle.kv_quantize(workloads.bf16_bits(k_cpu))
+    ovs = oracle.kv_quantize(workloads.bf16_bits(v_cpu))
+    nq = 4
+    t0 = time.perf_counter()
+    oracle.kv_attention(workloads.bf16_bits(qa_cpu), oks, ovs, T, D ** -0.5, q_idx=np.arange(nq))
+    oa_ms = (time.perf_counter() - t0) * 1e3 * Tq / nq
+    res["kv_attention_24x4096_over_65536"] = {
+        "H": H, "q_tokens": Tq, "kv_tokens": T, "D": D, "ms": round(a_ms, 4),
+        "TFLOP/s": round(flop_a / (a_ms * 1e-3) / 1e12, 1),
+        "frac_of_fp16_peak": round(flop_a / (a_ms * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
+        "workspace_bytes": wsa.numel(), "oracle_ms_est": round(oa_ms, 1),
+        "oracle_sample": "%d queries of every head" % nq, "oracle_threads": oracle.num_threads()}
+    log("attention", json.dumps(res["kv_attention_24x4096_over_65536"]))
+    del k, v, qk, qv, ok, ov, qa, oa, wsa, oks, ovs
+    torch.cuda.empty_cache()
+    # backward of the FFN up-projection: operands quantized along rows, dgrad and wgrad
+    a_cpu, w_cpu, dy_cpu = workloads.activations(3), workloads.weights(3), workloads.output_grads(3)
+    a, w, dy = a_cpu.to(dev), w_cpu.to(dev), dy_cpu.to(dev)
+    dyq, wtq, dytq, atq = nvfp4.quantize(dy), nvfp4.quantize_transposed(w), nvfp4.quantize_transposed(dy), \
+        nvfp4.quantize_transposed(a)
+    qt = lambda: nvfp4.quantize_transposed(dy, out=dytq[:2], s_g_out=dytq[2])
+    settle(torch, qt)
+    t_ms = time_calls(torch, qt, steps, warmup)
+    dx = nvfp4.gemm(dyq, wtq)
+    dw = nvfp4.gemm(dytq, atq)
+    dgrad = lambda: nvfp4.gemm(dyq, wtq, out=dx)
+    wgrad = lambda: nvfp4.gemm(dytq, atq, out=dw)
+    settle(torch, dgrad)
+    dx_ms = time_calls(torch, dgrad, steps, warmup)
+    dw_ms = time_calls(torch, wgrad, steps, warmup)
+    M3, N3 = dy.shape
+    K3 = w.shape[1]
+    fl = 2.0 * M3 * N3 * K3
+    dyn = workloads.bf16_bits(dy_cpu)
+    ncol = 256  # oracle: full amax + the columns of one 256-column sample
+    t0 = time.perf_counter()
+    g = oracle.global_scale(oracle.amax(dyn))
+    ta = time.perf_counter()
+    oracle.quantize_transposed(np.ascontiguousarray(dyn[:, :ncol]), g)
+    t1 = time.perf_counter()
+    ot_ms = (ta - t0) * 1e3 + (t1 - ta) * 1e3 * N3 / ncol
+    res["backward_ffn_up_16384x14336x3072"] = {
+        "quantize_transposed_dY_ms": round(t_ms, 4),
+        "quantize_transposed_dY_GB/s": round(dy.numel() * (B_AMAX + B_ENCODE) / (t_ms * 1e-3) / 1e9, 1),
+        "dgrad_ms": round(dx_ms, 4), "dgrad_TFLOP/s": round(fl / (dx_ms * 1e-3) / 1e12, 1),
+        "wgrad_ms": round(dw_ms, 4), "wgrad_TFLOP/s": round(fl / (dw_ms * 1e-3) / 1e12, 1),
+        "oracle_quantize_transposed_ms_est": round(ot_ms, 1),
+        "oracle_sample": "full amax, then %d of %d columns" % (ncol, N3), "oracle_threads": oracle.num_threads()}
+    log("backward", json.dumps(res["backward_ffn_up_16384x14336x3072"]))
     return res
 
 
