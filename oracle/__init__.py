@@ -25,7 +25,7 @@ _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force=False):
@@ -54,6 +54,7 @@ def _load():
         "orc_e2m1_value": (c_d, [c_i]),
         "orc_e4m3_value": (c_d, [c_i]),
         "orc_global_scale": (c_f, [c_f]),
+        "orc_global_scale_f64": (c_f, [c_d]),
         "orc_block_scale": (c_i, [c_d, c_f]),
         "orc_e2m1_code": (c_i, [c_d, c_d]),
         "orc_round_bf16": (ctypes.c_uint16, [c_d]),
@@ -64,6 +65,7 @@ def _load():
         "orc_gemm_ref": (c_i, [c_p, c_p, c_f, c_p, c_p, c_f, c_i64, c_i64, c_i64,
                                c_p, c_i64, c_p, c_i64, c_p, c_p]),
         "orc_kv_quantize": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
+        "orc_adaln": (c_i, [c_p, c_i, c_i64, c_i64, c_p, c_p, c_i64, c_d, c_p]),
         "orc_kv_dequantize": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i64, c_p]),
         "orc_kv_attention": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_d,
                                    c_p, c_i64, c_p, c_p]),
@@ -93,9 +95,11 @@ def _ptr(a):
 def _dtype_of(x):
     if x.dtype == np.float32:
         return F32
+    if x.dtype == np.float64:
+        return F64
     if x.dtype == np.uint16:
         return BF16
-    raise TypeError("oracle inputs are float32 arrays or uint16 bf16 bit patterns, got %s" % x.dtype)
+    raise TypeError("oracle inputs are float32 / float64 arrays or uint16 bf16 bit patterns, got %s" % x.dtype)
 
 
 def num_threads():
@@ -166,6 +170,23 @@ def quantize_transposed(x, s_g=None):
     training GEMMs too: landx.limxdynamics.com, sections on NVFP4 and on the training stage;
     d9249.github.io review, "Core idea / structure / operation"); s_g is the same as for x."""
     return quantize(np.ascontiguousarray(np.asarray(x).T), s_g)
+
+
+def adaln(x, shift, scale, rows_per_group, eps):
+    """fp64 y [rows, k] = LayerNorm(x) (no affine, biased variance, eps) * (1 + scale[g]) + shift[g],
+    g = row // rows_per_group; x float32 or bf16 bits [rows, k], shift / scale float32 [groups, k].
+    The adaLN half of the unified RoPE + adaLN kernel the yourai.pro page lists among the NVFP4
+    inference-path optimizations; quantize(y) gives what the fused adaLN quantizer computes."""
+    x = np.ascontiguousarray(x)
+    rows, k = x.shape
+    shift = np.ascontiguousarray(shift, np.float32)
+    scale = np.ascontiguousarray(scale, np.float32)
+    groups = (rows + rows_per_group - 1) // rows_per_group
+    assert shift.shape == (groups, k) and scale.shape == (groups, k)
+    y = np.empty((rows, k), np.float64)
+    _check(_load().orc_adaln(_ptr(x), _dtype_of(x), rows, k, _ptr(shift), _ptr(scale), rows_per_group,
+                             float(eps), _ptr(y)))
+    return y
 
 
 def dequantize(codes, scales, s_g, out="bf16"):

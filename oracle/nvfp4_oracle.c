@@ -42,6 +42,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* exact fp64 values (results of the oracle's own fp64 arithmetic) */
 #define ORC_OK 0
 #define ORC_ERR_NONFINITE (-1)
 #define ORC_ERR_SHAPE (-2)
@@ -68,6 +69,7 @@ static double bf16_to_double(uint16_t h) {
 
 static double load_elem(const void *x, int dtype, int64_t i) {
   if (dtype == ORC_F32) return (double)((const float *)x)[i];
+  if (dtype == ORC_F64) return ((const double *)x)[i];
   return bf16_to_double(((const uint16_t *)x)[i]);
 }
 
@@ -93,14 +95,19 @@ double orc_e4m3_value(int byte) {
  * ulp; the exact choice is made among it and its two neighbours by comparing
  * |f * 2688 - amax|, which is exact in fp64 (f*2688 has at most 29
  * significant bits and the two terms are within a factor of two). */
-float orc_global_scale(float amax) {
-  if (!(amax > 0.0f)) return 0.0f;
-  float c = (float)((double)amax / 2688.0);
+float orc_global_scale_f64(double amax);
+float orc_global_scale(float amax) { return orc_global_scale_f64((double)amax); }
+
+/* The same rounding for an fp64 amax: f * 2688 is exact (<= 36 bits) and
+ * within a factor of two of amax, so the difference is exact as well. */
+float orc_global_scale_f64(double amax) {
+  if (!(amax > 0.0)) return 0.0f;
+  float c = (float)(amax / 2688.0);
   float cand[3] = {nextafterf(c, 0.0f), c, nextafterf(c, INFINITY)};
   float best = cand[0];
   double best_err = INFINITY;
   for (int i = 0; i < 3; i++) {
-    double err = fabs((double)cand[i] * 2688.0 - (double)amax);
+    double err = fabs((double)cand[i] * 2688.0 - amax);
     uint32_t bits;
     memcpy(&bits, &cand[i], 4);
     if (err < best_err || (err == best_err && (bits & 1u) == 0)) {
@@ -171,6 +178,7 @@ uint16_t orc_round_bf16(double v) {
 
 /* amax = max |x| over n elements (exact). */
 int orc_amax(const void *x, int dtype, int64_t n, float *amax) {
+  if (dtype == ORC_F64) return ORC_ERR_SHAPE; /* the maximum of fp64 values need not be an fp32 value */
   double m = 0.0;
   for (int64_t i = 0; i < n; i++) {
     double v = load_elem(x, dtype, i);
@@ -209,15 +217,51 @@ int orc_quantize_with_scale(const void *x, int dtype, int64_t rows, int64_t k, f
   return bad ? ORC_ERR_NONFINITE : ORC_OK;
 }
 
-/* Full per-tensor quantization: amax -> s_g -> blocks. */
+/* Full per-tensor quantization: amax -> s_g -> blocks.  For fp64 inputs the
+ * amax is an fp64 value and s_g its exact rounding. */
 int orc_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
                  uint8_t *scales, float *s_g) {
   if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
-  float amax;
-  int st = orc_amax(x, dtype, rows * k, &amax);
-  if (st) return st;
-  *s_g = orc_global_scale(amax);
+  double m = 0.0;
+  for (int64_t i = 0; i < rows * k; i++) {
+    double v = load_elem(x, dtype, i);
+    if (!isfinite(v)) return ORC_ERR_NONFINITE;
+    if (fabs(v) > m) m = fabs(v);
+  }
+  *s_g = orc_global_scale_f64(m);
   return orc_quantize_with_scale(x, dtype, rows, k, *s_g, codes, scales);
+}
+
+/* adaLN of layer-normalized rows (the pages list a unified RoPE + adaLN kernel
+ * among the NVFP4 inference-path optimizations: yourai.pro news page), in
+ * fp64.  For row r of x [rows][k] and its group g = r / rows_per_group:
+ *   mu  = sum_d x[r][d] / k,   var = sum_d (x[r][d] - mu)^2 / k  (biased),
+ *   y[r][d] = (x[r][d] - mu) / sqrt(var + eps) * (1 + scale[g][d]) + shift[g][d],
+ * shift and scale fp32 [groups][k].  The result feeds orc_quantize as fp64. */
+int orc_adaln(const void *x, int dtype, int64_t rows, int64_t k, const float *shift, const float *scale,
+              int64_t rows_per_group, double eps, double *y) {
+  if (rows < 0 || k <= 0 || rows_per_group <= 0 || !(eps >= 0.0)) return ORC_ERR_SHAPE;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; r++) {
+    const int64_t g = r / rows_per_group;
+    double mu = 0.0, var = 0.0;
+    for (int64_t d = 0; d < k; d++) mu += load_elem(x, dtype, r * k + d);
+    mu /= (double)k;
+    for (int64_t d = 0; d < k; d++) {
+      double c = load_elem(x, dtype, r * k + d) - mu;
+      var += c * c;
+    }
+    var /= (double)k;
+    if (!isfinite(mu) || !isfinite(var)) bad = 1;
+    const double rstd = 1.0 / sqrt(var + eps);
+    for (int64_t d = 0; d < k; d++) {
+      const double c = load_elem(x, dtype, r * k + d) - mu;
+      y[r * k + d] = c * rstd * (1.0 + (double)scale[g * k + d]) + (double)shift[g * k + d];
+      if (!isfinite(y[r * k + d])) bad = 1;
+    }
+  }
+  return bad ? ORC_ERR_NONFINITE : ORC_OK;
 }
 
 /* y = RN_out(val(q) * val(s_b) * s_g); the product is exact in fp64
