@@ -49,6 +49,7 @@ GEMM_COUNTERS = {"sources_sha256": "4bfc004a09aef69b081d2c94230a5a0c8350863c54e2
 # Whole-pass HBM bytes per element (bf16 data, 4-bit code + one 8-bit scale per 16 elements).
 B_AMAX = 2.0
 B_ENCODE = 2.0 + 0.5 + 1.0 / 16
+B_ADALN = 2.0 + B_ENCODE  # fused adaLN quantizer: x read twice (amax pass, encode pass), codes + scales written
 B_DEQUANT = 0.5 + 1.0 / 16 + 2.0
 
 
@@ -212,7 +213,8 @@ def main():
 
 def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     """HBM throughput of the quantizer and the NVFP4 KV-cache round trip, the attention over
-    the packed cache, and the backward operands and GEMMs of the FFN up-projection."""
+    the packed cache, the backward operands and GEMMs of the FFN up-projection, and the
+    adaLN-fused quantizer."""
     res = {}
     # activation quantize of the FFN down-projection input (bf16 [16384, 14336], 470 MB)
     a4 = workloads.activations(4).to(dev)
@@ -286,6 +288,17 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
         "dgrad_dX_16384x3072x14336": {"ms": round(ms_dx, 4), "TFLOP/s": round(fl / (ms_dx * 1e-3) / 1e12, 1)},
         "wgrad_dW_14336x3072x16384": {"ms": round(ms_dw, 4), "TFLOP/s": round(fl / (ms_dw * 1e-3) / 1e12, 1)}}
     del w3, dy, dyq, wtq, dytq, atq, dx, dw
+    # adaLN fused into the quantizer: pre-norm hidden states [16384, 3072], 4 modulation groups
+    xa, sha, sca, rpg = workloads.adaln_inputs()
+    xa, sha, sca = xa.to(dev), sha.to(dev), sca.to(dev)
+    qa_ = nvfp4.adaln_quantize(xa, sha, sca, rpg)
+    ada = lambda: nvfp4.adaln_quantize(xa, sha, sca, rpg, out=qa_[:2], s_g_out=qa_[2])
+    settle(torch, ada)
+    ms_ad = time_calls(torch, ada, 10, 2)
+    res["adaln_quantize"] = {"shape": list(xa.shape), "groups": sha.shape[0], "ms": round(ms_ad, 4),
+                             "GB/s": round(xa.numel() * B_ADALN / (ms_ad * 1e-3) / 1e9, 1),
+                             "bytes_per_elem": B_ADALN}
+    del xa, sha, sca, qa_
     res["hbm_peak_GB/s"] = HBM_PEAK_GBS
     log("secondary", json.dumps(res))
     return res
@@ -431,6 +444,27 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         "oracle_quantize_transposed_ms_est": round(ot_ms, 1),
         "oracle_sample": "full amax, then %d of %d columns" % (ncol, N3), "oracle_threads": oracle.num_threads()}
     log("backward", json.dumps(res["backward_ffn_up_16384x14336x3072"]))
+    del a, w, dy, dyq, wtq, dytq, atq, dx, dw
+    torch.cuda.empty_cache()
+    # adaLN fused into the activation quantizer
+    x_cpu, sh_cpu, sc_cpu, rpg = workloads.adaln_inputs()
+    xa, sha, sca = x_cpu.to(dev), sh_cpu.to(dev), sc_cpu.to(dev)
+    qa_ = nvfp4.adaln_quantize(xa, sha, sca, rpg)
+    ada = lambda: nvfp4.adaln_quantize(xa, sha, sca, rpg, out=qa_[:2], s_g_out=qa_[2])
+    settle(torch, ada)
+    ad_ms = time_calls(torch, ada, steps, warmup)
+    nrow = 1024
+    xn = workloads.bf16_bits(x_cpu)
+    t0 = time.perf_counter()
+    yo = oracle.adaln(np.ascontiguousarray(xn[:nrow]), sh_cpu.numpy(), sc_cpu.numpy(), rpg, 1e-6)
+    oracle.quantize(yo)
+    oad_ms = (time.perf_counter() - t0) * 1e3 * x_cpu.shape[0] / nrow
+    res["adaln_quantize_16384x3072"] = {
+        "ms": round(ad_ms, 4), "GB/s": round(xa.numel() * B_ADALN / (ad_ms * 1e-3) / 1e9, 1),
+        "bytes_per_elem": B_ADALN, "oracle_ms_est": round(oad_ms, 1),
+        "oracle_sample": "%d of %d rows (adaLN + quantize)" % (nrow, x_cpu.shape[0]),
+        "oracle_threads": oracle.num_threads()}
+    log("adaln", json.dumps(res["adaln_quantize_16384x3072"]))
     return res
 
 

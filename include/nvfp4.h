@@ -132,6 +132,33 @@ nvfp4_status_t nvfp4_quantize_transposed(const void *x, int dtype, int64_t rows,
                                          void *stream);
 
 /*
+ * adaLN fused into the quantizer: quantize y [rows][k] to NVFP4 without
+ * writing y, where for row r in group g = r / rows_per_group
+ *   y[r][d] = (x[r][d] - mu_r) / sqrt(var_r + eps) * (1 + scale[g][d]) + shift[g][d],
+ *   mu_r, var_r the mean and biased variance of row r of x,
+ * computed in fp32 (row sums in a fixed order: deterministic).
+ *   x       [rows][k] dtype F32 or BF16, the pre-norm activations (tokens x
+ *           hidden), shift / scale fp32 [ceil(rows / rows_per_group)][k]
+ *           (one modulation per group of tokens, e.g. per frame chunk)
+ *   codes   [rows][k/2] u8 out      scales [rows][k/16] u8 out
+ *   s_g     [1] fp32: out with NVFP4_SCALE_COMPUTE (RN(max|y| / 2688)), in
+ *           with NVFP4_SCALE_GIVEN
+ * The codes equal nvfp4_quantize of y as computed here; against the exact
+ * (real-number) y they can differ only where an element or a block maximum
+ * lies within fp32 rounding of a decision boundary.  The yourai.pro page lists
+ * a unified RoPE + adaLN kernel among the NVFP4 inference-path
+ * optimizations; this is its adaLN half, fused with the activation
+ * quantization that follows it (the modulated activation never goes to HBM).
+ * Two passes over x (amax, then encode), the amax partials kept in the codes
+ * buffer.  Requires k % 16 == 0, 16 <= k <= 4096, rows_per_group >= 1,
+ * 0 <= eps finite; shift and scale 16-byte aligned.  rows == 0 is allowed
+ * (COMPUTE then writes s_g = 0).
+ */
+nvfp4_status_t nvfp4_adaln_quantize(const void *x, int dtype, int64_t rows, int64_t k, const float *shift,
+                                    const float *scale, int64_t rows_per_group, float eps, uint8_t *codes,
+                                    uint8_t *scales, float *s_g, int flags, void *stream);
+
+/*
  * Dequantize: y[r][i] = RN_ydtype(val(code) * val(scale) * s_g), y [rows][k]
  * of dtype F32 or BF16 (one rounding of the exact product).  Same shape
  * rules as nvfp4_quantize.  Per the d9249.github.io review (dequantization

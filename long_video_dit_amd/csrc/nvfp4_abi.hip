@@ -109,6 +109,22 @@ nvfp4_status_t nvfp4_quantize_transposed(const void* x, int dtype, int64_t rows,
   return from_hip(nvfp4::launch_encode_t(x, dtype, rows, cols, s_g, reinterpret_cast<uint32_t*>(codes_t), scales_t, s));
 }
 
+nvfp4_status_t nvfp4_adaln_quantize(const void* x, int dtype, int64_t rows, int64_t k, const float* shift,
+                                    const float* scale, int64_t rows_per_group, float eps, uint8_t* codes,
+                                    uint8_t* scales, float* s_g, int flags, void* stream) {
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  nvfp4_status_t st = check_matrix(rows, k, true);
+  if (st != NVFP4_OK) return st;
+  if (k > 4096 || rows_per_group <= 0 || !std::isfinite(eps) || !(eps >= 0.0f)) return NVFP4_ERR_SHAPE;
+  if (!s_g || (rows > 0 && (!x || !codes || !scales || !shift || !scale))) return NVFP4_ERR_NULL;
+  if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(shift, 16) ||
+      !aligned(scale, 16))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_adaln_quantize(x, dtype, rows, k, shift, scale, rows_per_group, eps, codes, scales,
+                                               s_g, flags == NVFP4_SCALE_COMPUTE, (hipStream_t)stream));
+}
+
 nvfp4_status_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t rows,
                                 int64_t k, void* y, int y_dtype, void* stream) {
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;

@@ -35,6 +35,14 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shm
 // units_per_group 8-element units, each run with its own s_g.
 hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group, int groups, uint32_t* partials,
                                int64_t partial_capacity, float* s_g, hipStream_t stream);
+// s_g[0] = RN_f32(max of P partials (fp32 bits) / 2688); P == 0 gives 0.
+hipError_t launch_finalize(const uint32_t* partials, int P, float* s_g, hipStream_t stream);
+// adaLN of layer-normalized rows fused into the quantizer (nvfp4_adaln.hip),
+// k % 16 == 0, k <= 4096.  compute_scale: s_g from the amax of y (partials
+// kept in the codes buffer), else the s_g stored at *s_g is used.
+hipError_t launch_adaln_quantize(const void* x, int dtype, int64_t rows, int64_t k, const float* shift,
+                                 const float* scale, int64_t rows_per_group, float eps, uint8_t* codes,
+                                 uint8_t* scales, float* s_g, bool compute_scale, hipStream_t stream);
 // Standalone per-tensor scale: zero the s_g slot, atomic-max the magnitude
 // bits into it, round in place (three kernels, no scratch).
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream);

@@ -378,6 +378,10 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group
                        (int)P, s_g);
 }
 
+hipError_t launch_finalize(const uint32_t* partials, int P, float* s_g, hipStream_t stream) {
+  return launch_kernel(finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partials, P, s_g);
+}
+
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(s_g);
   hipError_t e = launch_kernel(zero_slot_kernel, dim3(1), dim3(1), 0, stream, slot);

@@ -24,6 +24,7 @@ SIGNATURES = {
     "nvfp4_global_scale": (_I, [_P, _I, _I64, _I64, _P, _P]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P]),
     "nvfp4_quantize_transposed": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P]),
+    "nvfp4_adaln_quantize": (_I, [_P, _I, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _P, _I, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm_fused_act": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _P]),
@@ -124,6 +125,25 @@ def quantize_transposed(x, s_g=None, out=None, s_g_out=None):
         s_g = torch.empty(1, dtype=torch.float32, device=x.device) if s_g_out is None else s_g_out
     _call("nvfp4_quantize_transposed", _ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(s_g), flags,
           _stream(x.device))
+    return codes, scales, s_g
+
+
+def adaln_quantize(x, shift, scale, rows_per_group, eps=1e-6, s_g=None, out=None, s_g_out=None):
+    """NVFP4 of y = LayerNorm(x) * (1 + scale[g]) + shift[g] (g = row // rows_per_group) without
+    writing y: x [rows, k] float32/bfloat16, shift / scale float32 [groups, k] (device).
+    Returns (codes, scales, s_g) like quantize."""
+    _need_cuda(x, shift, scale)
+    rows, k = x.shape
+    if out is None:
+        codes = torch.empty(rows, k // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(rows, k // 16, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    flags = SCALE_COMPUTE if s_g is None else SCALE_GIVEN
+    if s_g is None:
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device) if s_g_out is None else s_g_out
+    _call("nvfp4_adaln_quantize", _ptr(x), _dt(x), rows, k, _ptr(shift), _ptr(scale), rows_per_group, float(eps),
+          _ptr(codes), _ptr(scales), _ptr(s_g), flags, _stream(x.device))
     return codes, scales, s_g
 
 

@@ -182,7 +182,7 @@ def adaln(x, shift, scale, rows_per_group, eps):
     shift = np.ascontiguousarray(shift, np.float32)
     scale = np.ascontiguousarray(scale, np.float32)
     groups = (rows + rows_per_group - 1) // rows_per_group
-    assert shift.shape == (groups, k) and scale.shape == (groups, k)
+    assert shift.shape[0] >= groups and shift.shape[1:] == (k,) and scale.shape == shift.shape
     y = np.empty((rows, k), np.float64)
     _check(_load().orc_adaln(_ptr(x), _dtype_of(x), rows, k, _ptr(shift), _ptr(scale), rows_per_group,
                              float(eps), _ptr(y)))

@@ -118,6 +118,23 @@ def test_validation_errors_launch_nothing():
     assert n.value == 7
     assert lib.kv_dequantize(buf, buf, buf, 4, -1, 128, buf, None) == nv.ERR_SHAPE
     assert lib.kv_dequantize(buf, buf, buf, 4, 16, 128, odd, None) == nv.ERR_ALIGN
+    qt = lib.nvfp4_quantize_transposed
+    assert qt(buf, 1, 24, 8, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # rows % 16
+    assert qt(buf, 1, 0, 8, buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert qt(buf, 7, 32, 8, buf, buf, buf, 0, None) == nv.ERR_DTYPE
+    assert qt(buf, 1, 32, 8, buf, buf, buf, 5, None) == nv.ERR_FLAGS
+    assert qt(None, 1, 32, 8, buf, buf, buf, 0, None) == nv.ERR_NULL
+    assert qt(buf, 1, 32, 8, odd, buf, buf, 0, None) == nv.ERR_ALIGN
+    ad = lib.nvfp4_adaln_quantize
+    assert ad(buf, 1, 4, 4112, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k > 4096
+    assert ad(buf, 1, 4, 40, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k % 16
+    assert ad(buf, 1, 4, 64, buf, buf, 0, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # rows_per_group
+    assert ad(buf, 1, 4, 64, buf, buf, 2, -1.0, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # eps
+    assert ad(buf, 1, 4, 64, buf, buf, 2, float("inf"), buf, buf, buf, 0, None) == nv.ERR_SHAPE
+    assert ad(buf, 1, 4, 64, None, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_NULL
+    assert ad(buf, 1, 4, 64, buf, odd, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_ALIGN
+    assert ad(buf, 3, 4, 64, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_DTYPE
+    assert ad(buf, 1, 4, 64, buf, buf, 2, 1e-6, buf, buf, buf, 9, None) == nv.ERR_FLAGS
 
 
 def test_attention_split_choice():

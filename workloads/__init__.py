@@ -23,6 +23,10 @@ torch.Generator seeded 1000*cfg + t, t = 0 activations/K, 1 weights/V,
   backward of a linear (configs 2-4): the output gradient dY bf16 [M, N] =
      2^-12 * s_m * N(0, 1), s_m = exp(0.5 z_m) per token m (t = 3, z: t = 4);
      with A and W of the config it feeds dX = dY W and dW = dY^T A
+  adaLN quantizer input (config 3 sizes): pre-norm hidden states x bf16
+     [16384, 3072] = m_t + std_k * N(0, 1) (std_k as config 3, per-token mean
+     m_t ~ N(0, 0.5^2), t = 5 / 6), modulation shift, scale fp32 [4, 3072]
+     ~ N(0, 0.5^2) (t = 7), one per group of 4096 tokens
 Sizes can be overridden (same recipe) for small parity cases.
 """
 import torch
@@ -83,6 +87,17 @@ def output_grads(cfg, M=None, N=None):
     g = torch.randn(M, N, generator=generator(cfg, 3), dtype=torch.float32)
     z = torch.randn(M, generator=generator(cfg, 4), dtype=torch.float32)
     return (g * (2.0 ** -12) * torch.exp(0.5 * z)[:, None]).to(torch.bfloat16)
+
+
+def adaln_inputs(M=16384, K=3072, rows_per_group=4096):
+    """(x bf16 [M, K], shift f32 [G, K], scale f32 [G, K], rows_per_group) of the fused adaLN quantizer."""
+    x = torch.randn(M, K, generator=generator(3, 5), dtype=torch.float32)
+    z = torch.randn(K, generator=generator(3, 2), dtype=torch.float32)
+    m = torch.randn(M, 1, generator=generator(3, 6), dtype=torch.float32) * 0.5
+    x = (x * torch.exp(0.5 * z)[None, :] + m).to(torch.bfloat16)
+    G = (M + rows_per_group - 1) // rows_per_group
+    mods = torch.randn(2, G, K, generator=generator(3, 7), dtype=torch.float32) * 0.5
+    return x, mods[0].contiguous(), mods[1].contiguous(), rows_per_group
 
 
 def kv_cache(H=None, T=None, D=None, sinks=4):
