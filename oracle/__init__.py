@@ -189,6 +189,26 @@ def adaln(x, shift, scale, rows_per_group, eps):
     return y
 
 
+def rope(x, positions, base=10000.0):
+    """Rotary position embedding of x [H, T, D] (float32 or bf16 bits) in fp64: for every pair of
+    adjacent dims (2i, 2i+1) and token t at position p = positions[t],
+        (y_2i, y_2i+1) = (x_2i cos(p th_i) - x_2i+1 sin(p th_i), x_2i sin(p th_i) + x_2i+1 cos(p th_i)),
+        th_i = base^(-2i / D).
+    The RoPE half of the unified RoPE + adaLN kernel the yourai.pro page lists among the NVFP4
+    inference-path optimizations; here it rotates new keys before they enter the NVFP4 cache."""
+    x = np.asarray(x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x
+    xf = xf.astype(np.float64)
+    H, T, D = xf.shape
+    th = np.power(float(base), -np.arange(0, D, 2, dtype=np.float64) / D)
+    ang = np.asarray(positions, np.float64)[:, None] * th[None, :]
+    c, s_ = np.cos(ang)[None], np.sin(ang)[None]
+    y = np.empty_like(xf)
+    y[..., 0::2] = xf[..., 0::2] * c - xf[..., 1::2] * s_
+    y[..., 1::2] = xf[..., 0::2] * s_ + xf[..., 1::2] * c
+    return y
+
+
 def dequantize(codes, scales, s_g, out="bf16"):
     """-> bf16 bit patterns (uint16) or float32 [rows, k]."""
     codes = np.ascontiguousarray(codes, np.uint8)
