@@ -259,7 +259,14 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
                            "workspace_bytes": wsa.numel(),
                            "TFLOP/s": round(flop_a / (ms_a * 1e-3) / 1e12, 1),
                            "frac_of_fp16_peak": round(flop_a / (ms_a * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4)}
-    del qa, oa, wsa
+    # RoPE fused into the append: the chunk's 4096 new keys per head rotated into the cache tail
+    kn = qa.clone()
+    ra = lambda: nvfp4.kv_rope_quantize_append(kn, qk, T - Tq)
+    settle(torch, ra, 0.2)
+    ms_r = time_calls(torch, ra, 10, 2)
+    res["kv_rope_append"] = {"heads": H, "tokens_new": Tq, "head_dim": D, "ms": round(ms_r, 4),
+                             "GB/s": round(kn.numel() * (2 + 0.5625) / (ms_r * 1e-3) / 1e9, 1)}
+    del qa, oa, wsa, kn
     ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}

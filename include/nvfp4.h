@@ -228,6 +228,33 @@ nvfp4_status_t kv_quantize_append(const void *kv_new, int64_t heads, int64_t tok
                                   int64_t cache_tokens, int64_t token_offset, void *stream);
 
 /*
+ * Rotary position embedding fused into the KV append: new keys k_new
+ * [heads][tokens_new][head_dim] bf16 are rotated and quantized into rows
+ * token_offset .. token_offset + tokens_new - 1 of each head of the cache
+ * (codes [heads][cache_tokens][head_dim/2], scales [heads][cache_tokens]
+ * [head_dim/16]) under the frozen per-head scales in head_scales [heads],
+ * as kv_quantize_append does for unrotated rows.  For new token t at
+ * position p = positions[t] (device int32 [tokens_new]; NULL: p =
+ * token_offset + t) and each pair of adjacent dims (2i, 2i + 1):
+ *   (y_2i, y_2i+1) = (x_2i cos(p th_i) - x_2i+1 sin(p th_i),
+ *                     x_2i sin(p th_i) + x_2i+1 cos(p th_i)),  th_i = rope_base^(-2i / head_dim).
+ * The angle p th_i is formed and reduced to [-pi, pi] in fp64; the sine,
+ * cosine and rotation are fp32.  Against the exact rotation the codes can
+ * differ only where an element or a block maximum lies within that fp32
+ * error of a decision boundary.  The yourai.pro page lists a unified RoPE +
+ * adaLN kernel and in-place updates of the quantized cache among the NVFP4
+ * inference-path optimizations; this is the RoPE half, fused with the append
+ * (the rotated keys never go to HBM in bf16).  Requires head_dim % 16 == 0
+ * and 256 % (head_dim / 8) == 0 (head_dim 16 .. 2048, powers of two), a
+ * finite rope_base > 0, 0 <= token_offset, token_offset + tokens_new <=
+ * cache_tokens; tokens_new == 0 is a no-op.
+ */
+nvfp4_status_t kv_rope_quantize_append(const void *k_new, int64_t heads, int64_t tokens_new, int64_t head_dim,
+                                       const int32_t *positions, float rope_base, const float *head_scales,
+                                       uint8_t *codes, uint8_t *scales, int64_t cache_tokens,
+                                       int64_t token_offset, void *stream);
+
+/*
  * NVFP4 KV cache dequantize to bf16 [heads][tokens][head_dim]:
  *   out = RN_bf16(val(code) * val(scale) * head_scales[h]).
  * The "parallel dequantization" of the d9249.github.io review (section

@@ -218,6 +218,24 @@ nvfp4_status_t kv_quantize_append(const void* kv_new, int64_t heads, int64_t tok
                                        cache_tokens * head_dim / 8, token_offset * head_dim / 8));
 }
 
+nvfp4_status_t kv_rope_quantize_append(const void* k_new, int64_t heads, int64_t tokens_new, int64_t head_dim,
+                                       const int32_t* positions, float rope_base, const float* head_scales,
+                                       uint8_t* codes, uint8_t* scales, int64_t cache_tokens, int64_t token_offset,
+                                       void* stream) {
+  nvfp4_status_t st = check_kv(heads, tokens_new, head_dim);
+  if (st == NVFP4_OK) st = check_kv(heads, cache_tokens, head_dim);
+  if (st != NVFP4_OK) return st;
+  if (256 % (head_dim / 8) != 0 || !std::isfinite(rope_base) || !(rope_base > 0.0f)) return NVFP4_ERR_SHAPE;
+  if (token_offset < 0 || token_offset > cache_tokens || tokens_new > cache_tokens - token_offset) return NVFP4_ERR_SHAPE;
+  if (!head_scales || (tokens_new > 0 && (!k_new || !codes || !scales))) return NVFP4_ERR_NULL;
+  if (!aligned(head_scales, 4) || !aligned(k_new, 16) || !aligned(codes, 16) || !aligned(scales, 4) ||
+      !aligned(positions, 4))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_kv_rope_append(k_new, heads, tokens_new, head_dim, positions, (double)rope_base,
+                                               head_scales, codes, scales, cache_tokens, token_offset,
+                                               (hipStream_t)stream));
+}
+
 nvfp4_status_t kv_dequantize(const uint8_t* codes, const uint8_t* scales, const float* head_scales, int64_t heads,
                              int64_t tokens, int64_t head_dim, void* kv_out, void* stream) {
   nvfp4_status_t st = check_kv(heads, tokens, head_dim);

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <tuple>
 #include <utility>
 
@@ -43,6 +44,12 @@ hipError_t launch_finalize(const uint32_t* partials, int P, float* s_g, hipStrea
 hipError_t launch_adaln_quantize(const void* x, int dtype, int64_t rows, int64_t k, const float* shift,
                                  const float* scale, int64_t rows_per_group, float eps, uint8_t* codes,
                                  uint8_t* scales, float* s_g, bool compute_scale, hipStream_t stream);
+// RoPE of new keys fused into the NVFP4 KV append (nvfp4_rope.hip), bf16 in,
+// 256 % (head_dim / 8) == 0; positions NULL: token_offset + t.
+hipError_t launch_kv_rope_append(const void* k_new, int64_t heads, int64_t tokens_new, int64_t head_dim,
+                                 const int32_t* positions, double rope_base, const float* head_scales,
+                                 uint8_t* codes, uint8_t* scales, int64_t cache_tokens, int64_t token_offset,
+                                 hipStream_t stream);
 // Standalone per-tensor scale: zero the s_g slot, atomic-max the magnitude
 // bits into it, round in place (three kernels, no scratch).
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream);

@@ -29,8 +29,9 @@ SIGNATURES = {
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm_fused_act": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _P]),
     "kv_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
-    "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kv_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P]),
+    "kv_rope_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _P]),
+    "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kv_attention": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                           ctypes.c_size_t, _P]),
     "kv_attention_workspace_size": (_I, [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
@@ -226,6 +227,20 @@ def kv_dequantize(codes, scales, head_scales, out=None):
     y = torch.empty(H, T, D, dtype=torch.bfloat16, device=codes.device) if out is None else out
     _call("kv_dequantize", _ptr(codes), _ptr(scales), _ptr(head_scales), H, T, D, _ptr(y), _stream(codes.device))
     return y
+
+
+def kv_rope_quantize_append(k_new, cache, token_offset, positions=None, base=10000.0):
+    """Rotate new keys k_new bf16 [H, Tn, D] with RoPE (positions int32 [Tn] on the device, default
+    token_offset + t) and quantize them in place into rows token_offset .. of the NVFP4 cache
+    (codes [H, T, D/2], scales [H, T, D/16], head_scales [H]) under its frozen head scales."""
+    codes, scales, hs = cache
+    _need_cuda(k_new, codes, scales, hs, positions)
+    H, Tn, D = k_new.shape
+    if positions is not None and positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    _call("kv_rope_quantize_append", _ptr(k_new), H, Tn, D, _ptr(positions), float(base), _ptr(hs), _ptr(codes),
+          _ptr(scales), codes.shape[1], token_offset, _stream(k_new.device))
+    return cache
 
 
 def kv_attention_workspace_size(heads, q_tokens, kv_tokens, head_dim=128):

@@ -74,3 +74,52 @@ def c_to_f64(c_dev):
     if c_dev.dtype == torch.bfloat16:
         return bf16_to_f64(c_dev.cpu().view(torch.int16).numpy().view(np.uint16))
     return c_dev.cpu().numpy().astype(np.float64)
+
+
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+E4M3 = np.array([oracle.e4m3_value(b) for b in range(127)], np.float64)
+
+
+def _unpack_codes(codes):
+    lo, hi = codes & 0xF, codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def check_quant_near_exact(codes, scales, y, tau, s_g, label):
+    """GPU codes / scales (device tensors) of values the kernel computed in fp32, against the
+    oracle's exact quantization of the fp64 values y with the same s_g: a scale byte or code may
+    differ only where the exact block maximum or element lies within tau (per element) of the
+    boundary between the two neighbouring values, and such elements must be rare."""
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    oc, os_, _ = oracle.quantize(y, np.float32(s_g))
+    rows, k = y.shape
+    sg = float(np.float32(s_g))
+    amax_b = np.abs(y).reshape(rows, k // 16, 16).max(axis=2)
+    tau_b = tau.reshape(rows, k // 16, 16).max(axis=2)
+    bad_b = np.argwhere(gs != os_)
+    for r, b in bad_b:
+        lo, hi = sorted((int(gs[r, b]), int(os_[r, b])))
+        assert hi == lo + 1, "%s: block (%d,%d) scale bytes %d / %d not adjacent" % (label, r, b, gs[r, b], os_[r, b])
+        mid = 0.5 * (E4M3[lo] + E4M3[hi]) * 6 * sg
+        assert abs(amax_b[r, b] - mid) <= tau_b[r, b], "%s: block (%d,%d) scale differs away from a boundary" % (
+            label, r, b)
+    same_block = np.repeat(gs == os_, 16, axis=1)
+    gq, oq = _unpack_codes(gc), _unpack_codes(oc)
+    diff = np.argwhere((gq != oq) & same_block)
+    S = np.repeat(E4M3[os_.astype(int)] * sg, 16, axis=1)
+    for r, d in diff:
+        m1, m2 = int(gq[r, d]) & 7, int(oq[r, d]) & 7
+        v = abs(y[r, d])
+        if m1 == m2:  # sign only: a value within tau of zero that rounds to magnitude 0
+            assert m1 == 0 and v <= tau[r, d], "%s: (%d,%d) sign differs" % (label, r, d)
+            continue
+        lo, hi = sorted((m1, m2))
+        same_sign = (int(gq[r, d]) >> 3) == (int(oq[r, d]) >> 3)
+        assert hi == lo + 1 and (same_sign or lo == 0), "%s: (%d,%d) codes %#x / %#x not neighbours" % (
+            label, r, d, gq[r, d], oq[r, d])
+        mid = 0.5 * (E2M1[lo] + E2M1[hi]) * S[r, d]
+        assert abs(v - mid) <= tau[r, d], "%s: (%d,%d) code %#x vs %#x away from a boundary (|y| %.9g, mid %.9g)" % (
+            label, r, d, gq[r, d], oq[r, d], v, mid)
+    n_diff = len(diff) + 16 * len(bad_b)
+    log(label, "elements off the exact rounding: %d of %d (%d blocks)" % (len(diff), y.size, len(bad_b)))
+    assert n_diff <= 1e-4 * y.size + 16

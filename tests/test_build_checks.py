@@ -125,6 +125,14 @@ def test_validation_errors_launch_nothing():
     assert qt(buf, 1, 32, 8, buf, buf, buf, 5, None) == nv.ERR_FLAGS
     assert qt(None, 1, 32, 8, buf, buf, buf, 0, None) == nv.ERR_NULL
     assert qt(buf, 1, 32, 8, odd, buf, buf, 0, None) == nv.ERR_ALIGN
+    ra = lib.kv_rope_quantize_append
+    assert ra(buf, 2, 8, 96, None, 1e4, buf, buf, buf, 64, 0, None) == nv.ERR_SHAPE  # 256 % (96 / 8) != 0
+    assert ra(buf, 2, 8, 128, None, 0.0, buf, buf, buf, 64, 0, None) == nv.ERR_SHAPE  # base
+    assert ra(buf, 2, 8, 128, None, float("nan"), buf, buf, buf, 64, 0, None) == nv.ERR_SHAPE
+    assert ra(buf, 2, 8, 128, None, 1e4, buf, buf, buf, 64, 57, None) == nv.ERR_SHAPE  # past the cache
+    assert ra(buf, 2, 8, 128, None, 1e4, None, buf, buf, 64, 0, None) == nv.ERR_NULL
+    assert ra(buf, 2, 8, 128, odd, 1e4, buf, buf, buf, 64, 0, None) == nv.ERR_ALIGN  # positions
+    assert ra(buf, 2, 0, 128, None, 1e4, buf, buf, buf, 64, 64, None) == nv.OK  # empty append
     ad = lib.nvfp4_adaln_quantize
     assert ad(buf, 1, 4, 4112, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k > 4096
     assert ad(buf, 1, 4, 40, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k % 16

@@ -17,13 +17,9 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import dev, f32_bits, log, oracle_input
+from tests.gpu_helpers import check_quant_near_exact, dev, f32_bits, log, oracle_input
 
 pytestmark = pytest.mark.gpu
-
-E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
-E4M3 = np.array([oracle.e4m3_value(b) for b in range(127)], np.float64)
-
 
 def _nv():
     from long_video_dit_amd import nvfp4
@@ -43,48 +39,6 @@ def _tau(x64, shift, scale, rpg, eps):
     return 4 * (np.abs(a1) * (rstd * e_mu + np.abs(t) * e_r) + (np.abs(t * a1) + np.abs(b)) * 2.0 ** -23)
 
 
-def _unpack(codes):
-    lo, hi = codes & 0xF, codes >> 4
-    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
-
-
-def _check(gpu, y, tau, s_g, label):
-    """gpu (codes, scales) vs the oracle's exact quantization of y with the same s_g."""
-    gc, gs = gpu[0].cpu().numpy(), gpu[1].cpu().numpy()
-    oc, os_, _ = oracle.quantize(y, np.float32(s_g))
-    rows, k = y.shape
-    sg = float(np.float32(s_g))
-    amax_b = np.abs(y).reshape(rows, k // 16, 16).max(axis=2)
-    tau_b = tau.reshape(rows, k // 16, 16).max(axis=2)
-    bad_b = np.argwhere(gs != os_)
-    for r, b in bad_b:
-        lo, hi = sorted((int(gs[r, b]), int(os_[r, b])))
-        assert hi == lo + 1, "%s: block (%d,%d) scale bytes %d / %d not adjacent" % (label, r, b, gs[r, b], os_[r, b])
-        mid = 0.5 * (E4M3[lo] + E4M3[hi]) * 6 * sg
-        assert abs(amax_b[r, b] - mid) <= tau_b[r, b], "%s: block (%d,%d) scale differs away from a boundary" % (
-            label, r, b)
-    same_block = np.repeat(gs == os_, 16, axis=1)
-    gq, oq = _unpack(gc), _unpack(oc)
-    diff = np.argwhere((gq != oq) & same_block)
-    S = np.repeat(E4M3[os_.astype(int)] * sg, 16, axis=1)
-    for r, d in diff:
-        m1, m2 = int(gq[r, d]) & 7, int(oq[r, d]) & 7
-        v = abs(y[r, d])
-        if m1 == m2:  # sign only: a value within tau of zero that rounds to magnitude 0
-            assert m1 == 0 and v <= tau[r, d], "%s: (%d,%d) sign differs" % (label, r, d)
-            continue
-        lo, hi = sorted((m1, m2))
-        same_sign = (int(gq[r, d]) >> 3) == (int(oq[r, d]) >> 3)
-        assert hi == lo + 1 and (same_sign or lo == 0), "%s: (%d,%d) codes %#x / %#x not neighbours" % (
-            label, r, d, gq[r, d], oq[r, d])
-        mid = 0.5 * (E2M1[lo] + E2M1[hi]) * S[r, d]
-        assert abs(v - mid) <= tau[r, d], "%s: (%d,%d) code %#x vs %#x away from a boundary (|y| %.9g, mid %.9g)" % (
-            label, r, d, gq[r, d], oq[r, d], v, mid)
-    n_diff = len(diff) + 16 * len(bad_b)
-    log(label, "elements off the exact rounding: %d of %d (%d blocks)" % (len(diff), y.size, len(bad_b)))
-    assert n_diff <= 1e-4 * y.size + 16
-
-
 def _run(x_cpu, shift, scale, rpg, eps, label, check_scale=True):
     nv = _nv()
     y = oracle.adaln(oracle_input(x_cpu), shift.numpy(), scale.numpy(), rpg, eps)
@@ -95,7 +49,7 @@ def _run(x_cpu, shift, scale, rpg, eps, label, check_scale=True):
     given = nv.adaln_quantize(xd, shd, scd, rpg, eps, s_g=torch.tensor([float(s_o)], device=dev()))
     comp = nv.adaln_quantize(xd, shd, scd, rpg, eps)
     torch.cuda.synchronize()
-    _check(given, y, tau, s_o, label)
+    check_quant_near_exact(given[0], given[1], y, tau, s_o, label)
     g = comp[2].cpu().numpy()[0]
     if check_scale:
         if f32_bits(g) != f32_bits(s_o):
