@@ -15,9 +15,11 @@
 // formed and reduced to [-pi, pi] in fp64 (th_i in fp64, Cody-Waite with a
 // two-part 2 pi), and only the reduced angle goes to sincosf.
 //
-// Layout: one lane per 8-element unit of one token; D / 8 divides 256, so in
-// the grid-stride loop every thread keeps the same unit w of head_dim and its
-// four th_i are computed once.  Lanes 2j and 2j + 1 hold one 16-element block.
+// Layout: one lane per 8-element unit of one token, looping over 4 heads
+// with that token's sines and cosines (they do not depend on the head); D / 8
+// divides 256, so in the grid-stride loop every thread keeps the same unit w
+// of head_dim and its four th_i are computed once.  Lanes 2j and 2j + 1 hold
+// one 16-element block.
 #include <hip/hip_runtime.h>
 
 #include "nvfp4_device.h"
@@ -28,50 +30,57 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kRopeThreads = 256;
+constexpr int kRopeHeads = 4;  // heads per workgroup (blockIdx.y): their loads are issued together
 constexpr double kTwoPiHi = 6.283185307179586232;       // RN_f64(2 pi)
 constexpr double kTwoPiLo = 2.4492935982947063545e-16;   // 2 pi - kTwoPiHi
 constexpr double kInvTwoPi = 0.15915494309189533577;  // only picks the multiple of 2 pi
 
 __global__ __launch_bounds__(kRopeThreads) void rope_encode_kernel(
-    const uint16_t* __restrict__ k_new, int64_t tokens_new, int D, const int32_t* __restrict__ positions,
+    const uint16_t* __restrict__ k_new, int heads, int64_t tokens_new, int D, const int32_t* __restrict__ positions,
     int64_t token_offset, double log2_base, const float* __restrict__ head_scales, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t cache_tokens) {
-  const int h = blockIdx.y;
-  const EncodeConsts c = make_encode_consts(head_scales[h]);
   const int upt = D / 8;  // units per token; divides the stride below
   const int w = threadIdx.x % upt;
   double th[4];
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) th[jj] = exp2(-(double)(8 * w + 2 * jj) / (double)D * log2_base);
   const int64_t units = tokens_new * upt;
-  const uint16_t* xh = k_new + (int64_t)h * tokens_new * D;
-  uint32_t* ch = codes + ((int64_t)h * cache_tokens + token_offset) * upt;
-  uint8_t* sh = scales + ((int64_t)h * cache_tokens + token_offset) * (upt / 2);
   for (int64_t u = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x; u < units;
        u += (int64_t)gridDim.x * kRopeThreads) {  // pairs of lanes enter and leave together (units even)
     const int64_t t = u / upt;
     const double p = positions ? (double)positions[t] : (double)(token_offset + t);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xh + 8 * u);
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-    float y[8];
+    float sn[4], cs[4];  // the rotation of this token's unit, shared by every head
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) {
-      const float x0 = __uint_as_float(wd[jj] << 16), x1 = __uint_as_float(wd[jj] & 0xffff0000u);
       const double ang = p * th[jj];
       const double n = rint(ang * kInvTwoPi);
       const double r = __builtin_fma(-n, kTwoPiLo, __builtin_fma(-n, kTwoPiHi, ang));
-      float sn, cs;
-      sincosf((float)r, &sn, &cs);
-      y[2 * jj] = __builtin_fmaf(x0, cs, -(x1 * sn));
-      y[2 * jj + 1] = __builtin_fmaf(x0, sn, x1 * cs);
+      sincosf((float)r, &sn[jj], &cs[jj]);
     }
-    float am = 0.0f;
+    const int h0 = blockIdx.y * kRopeHeads;
 #pragma unroll
-    for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(y[i]));
-    am = __builtin_fmaxf(am, __shfl_xor(am, 1));
-    const uint32_t sb = encode_scale(am, c);
-    ch[u] = encode8(y, sb, c);
-    if ((threadIdx.x & 1) == 0) sh[u >> 1] = (uint8_t)sb;
+    for (int hh = 0; hh < kRopeHeads; hh++) {
+      const int h = h0 + hh;
+      if (h >= heads) break;  // uniform
+      const EncodeConsts c = make_encode_consts(head_scales[h]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(k_new + ((int64_t)h * tokens_new) * D + 8 * u);
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      float y[8];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float x0 = __uint_as_float(wd[jj] << 16), x1 = __uint_as_float(wd[jj] & 0xffff0000u);
+        y[2 * jj] = __builtin_fmaf(x0, cs[jj], -(x1 * sn[jj]));
+        y[2 * jj + 1] = __builtin_fmaf(x0, sn[jj], x1 * cs[jj]);
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(y[i]));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 1));
+      const uint32_t sb = encode_scale(am, c);
+      const int64_t row = (int64_t)h * cache_tokens + token_offset;  // this head's first appended row
+      codes[row * upt + u] = encode8(y, sb, c);
+      if ((threadIdx.x & 1) == 0) scales[row * (upt / 2) + (u >> 1)] = (uint8_t)sb;
+    }
   }
 }
 
@@ -84,10 +93,11 @@ hipError_t launch_kv_rope_append(const void* k_new, int64_t heads, int64_t token
   if (tokens_new == 0) return hipSuccess;
   const int64_t units = tokens_new * head_dim / 8;
   const int64_t want = (units + kRopeThreads - 1) / kRopeThreads;
-  const int64_t cap = std::max<int64_t>(1, (int64_t)device_cu_count() * 16 / heads);
-  const dim3 grid((unsigned)std::min(want, cap), (unsigned)heads);
-  return launch_kernel(rope_encode_kernel, grid, dim3(kRopeThreads), 0, stream, (const uint16_t*)k_new, tokens_new,
-                       (int)head_dim, positions, token_offset, std::log2(rope_base), head_scales,
+  const int64_t hgroups = (heads + kRopeHeads - 1) / kRopeHeads;
+  const int64_t cap = std::max<int64_t>(1, (int64_t)device_cu_count() * 16 / hgroups);
+  const dim3 grid((unsigned)std::min<int64_t>(want, cap), (unsigned)hgroups);
+  return launch_kernel(rope_encode_kernel, grid, dim3(kRopeThreads), 0, stream, (const uint16_t*)k_new, (int)heads,
+                       tokens_new, (int)head_dim, positions, token_offset, std::log2(rope_base), head_scales,
                        reinterpret_cast<uint32_t*>(codes), scales, cache_tokens);
 }
 
