@@ -415,6 +415,22 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         "workspace_bytes": wsa.numel(), "oracle_ms_est": round(oa_ms, 1),
         "oracle_sample": "%d queries of every head" % nq, "oracle_threads": oracle.num_threads()}
     log("attention", json.dumps(res["kv_attention_24x4096_over_65536"]))
+    # RoPE fused into the append: the chunk's 4096 new keys per head rotated into the cache tail
+    kn = qa.clone()
+    ra = lambda: nvfp4.kv_rope_quantize_append(kn, qk, T - Tq)
+    settle(torch, ra, 0.2)
+    r_ms = time_calls(torch, ra, steps, warmup)
+    nh = 1
+    t0 = time.perf_counter()
+    yr = oracle.rope(workloads.bf16_bits(qa_cpu[:nh]), np.arange(T - Tq, T), 10000.0)
+    oracle.quantize(yr[0], np.float32(oks[2][0]))
+    or_ms = (time.perf_counter() - t0) * 1e3 * H / nh
+    res["kv_rope_append_24x4096"] = {
+        "ms": round(r_ms, 4), "GB/s": round(kn.numel() * (2 + 0.5625) / (r_ms * 1e-3) / 1e9, 1),
+        "oracle_ms_est": round(or_ms, 1), "oracle_sample": "%d of %d heads" % (nh, H),
+        "oracle_threads": oracle.num_threads()}
+    log("rope append", json.dumps(res["kv_rope_append_24x4096"]))
+    del kn
     del k, v, qk, qv, ok, ov, qa, oa, wsa, oks, ovs
     torch.cuda.empty_cache()
     # backward of the FFN up-projection: operands quantized along rows, dgrad and wgrad

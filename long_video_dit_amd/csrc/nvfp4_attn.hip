@@ -19,7 +19,8 @@
 //                   ONE query (16 of a 32-token tile; the other 16 sit in lane
 //                   l ^ 32): the row maximum needs one cross-half exchange;
 //   online softmax  exp2 of scores pre-multiplied by scale * s_gK * log2(e),
-//                   running max m and per-lane partial sums l in fp32;
+//                   a lazily updated running max m (moved only when a block
+//                   exceeds it by 2^8) and per-lane partial sums l in fp32;
 //   O^T += V^T P^T  v_mfma_f32_32x32x16_f16 (P rounded to fp16, exact fp16
 //                   V).  The A operand needs 8 consecutive tokens of one
 //                   head-dim column per lane while the cache is token-major:
@@ -62,6 +63,7 @@ constexpr int kAQW = 32;         // queries per wave
 constexpr int kAW = 8;           // waves per workgroup
 constexpr int kABM = kAW * kAQW; // queries per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;  // log2 of the largest probability before the maximum moves
 
 struct AttnSmem {
   uint8_t k[kABN * 256];
@@ -168,7 +170,10 @@ __device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], float c, int
   }
   bm *= c;
   bm = fmaxf(bm, __shfl_xor(bm, 32));
-  const float m_new = fmaxf(m, bm);
+  // Lazy maximum: the reference point only moves when the block maximum
+  // exceeds it by more than 2^8, so probabilities stay <= 256 (fp16 keeps its
+  // 2^-11 relative rounding there) and the output rescale is rare.
+  const float m_new = bm > m + kLazyLog2 ? bm : m;
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
   m = m_new;
 #pragma unroll
