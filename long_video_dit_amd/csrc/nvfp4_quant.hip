@@ -244,16 +244,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
 // x [rows][cols] -> the NVFP4 form of x^T: codes [cols][rows / 2], scales
 // [cols][rows / 16], blocks of 16 consecutive rows of one column (the layout
 // the backward GEMMs contract over: dgrad over the output features of W,
-// wgrad over tokens).  One workgroup per tile of 256 rows x 64 columns; lane
-// (c4 = lane % 16, rb = 4 wave + lane / 16) owns columns 4 c4 .. 4 c4 + 3 and
-// rows 16 rb .. 16 rb + 15 of the tile, i.e. four whole blocks, so the block
-// maximum needs no lane exchange.  Loads: the 16 lanes of one rb read one
-// contiguous row segment (128 B of bf16).  Codes and scale bytes are staged
+// wgrad over tokens).  One 512-thread workgroup per tile of 256 rows x 128
+// columns; lane
+// (c4 = lane % 16 + 16 (wave / 4), rb = 4 (wave % 4) + lane / 16) owns
+// columns 4 c4 .. 4 c4 + 3 and rows 16 rb .. 16 rb + 15 of the tile, i.e.
+// four whole blocks, so the block maximum needs no lane exchange.  Loads: the
+// 16 lanes of one rb read 128 contiguous bytes of bf16, and a tile reads
+// 256-byte row segments.  Codes and scale bytes are staged
 // in LDS per tile and stored column by column, 16 lanes x 8 B = one 128-byte
 // line of codes per column and 16 scale bytes per column, instead of 32-byte
 // pieces of 16 columns per instruction.  Same rounding helpers as the
 // row-wise pass, so the result is bit-identical to quantizing x^T.
-constexpr int kTR = 256, kTC = 64;
+constexpr int kTR = 256, kTC = 128, kTThreads = 512;
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* __restrict__ p, float (&f)[4]);
@@ -277,7 +279,7 @@ __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_flo
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
 template <typename T, bool kVec>
-__global__ __launch_bounds__(kThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                             const float* __restrict__ s_g,
                                                             uint32_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void encode_t_kernel(const T* __restrict_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tiles_c = (cols + kTC - 1) / kTC;
   const int64_t tr0 = (int64_t)(blockIdx.x / tiles_c) * kTR, tc0 = (int64_t)(blockIdx.x % tiles_c) * kTC;
-  const int rb = 4 * wave + (lane >> 4), c4 = lane & 15;
+  const int rb = 4 * (wave & 3) + (lane >> 4), c4 = (lane & 15) + 16 * (wave >> 2);
   const int64_t r0 = tr0 + 16 * rb, col0 = tc0 + 4 * c4;
   if (r0 < rows && col0 < cols) {  // rows % 16 == 0: a block is wholly in or out
     float f[4][16];
@@ -325,14 +327,15 @@ __global__ __launch_bounds__(kThreads) void encode_t_kernel(const T* __restrict_
   // Codes: 16 lanes per column, lane p stores rows 16 p .. 16 p + 15 (8 B).
   const int64_t words_per_col = rows / 8;
 #pragma unroll
-  for (int it = 0; it < kTC * 16 / kThreads; it++) {
-    const int idx = it * kThreads + threadIdx.x, cl = idx >> 4, p = idx & 15;
+  for (int it = 0; it < kTC * 16 / kTThreads; it++) {
+    const int idx = it * kTThreads + threadIdx.x, cl = idx >> 4, p = idx & 15;
     if (tc0 + cl < cols && tr0 + 16 * p < rows)
       *reinterpret_cast<u32x2*>(codes + (tc0 + cl) * words_per_col + tr0 / 8 + 2 * p) =
           *reinterpret_cast<const u32x2*>(&sc[cl][2 * p]);
   }
   // Scale bytes: 4 lanes per column, 4 bytes each when aligned.
   {
+    static_assert(kTC * 4 == kTThreads, "one scale word per thread");
     const int cl = threadIdx.x >> 2, p = threadIdx.x & 3;
     if (tc0 + cl < cols) {
       uint8_t* dst = scales + (tc0 + cl) * (rows / 16) + tr0 / 16 + 4 * p;
@@ -419,13 +422,13 @@ hipError_t launch_encode_t(const void* x, int dtype, int64_t rows, int64_t cols,
   const dim3 grid((unsigned)tiles);
   const bool vec = cols % 4 == 0;
   if (dtype == kDtypeF32)
-    return vec ? launch_kernel(encode_t_kernel<float, true>, grid, dim3(kThreads), 0, stream, (const float*)x, rows,
+    return vec ? launch_kernel(encode_t_kernel<float, true>, grid, dim3(kTThreads), 0, stream, (const float*)x, rows,
                                cols, s_g, codes, scales)
-               : launch_kernel(encode_t_kernel<float, false>, grid, dim3(kThreads), 0, stream, (const float*)x, rows,
+               : launch_kernel(encode_t_kernel<float, false>, grid, dim3(kTThreads), 0, stream, (const float*)x, rows,
                                cols, s_g, codes, scales);
-  return vec ? launch_kernel(encode_t_kernel<uint16_t, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x,
+  return vec ? launch_kernel(encode_t_kernel<uint16_t, true>, grid, dim3(kTThreads), 0, stream, (const uint16_t*)x,
                              rows, cols, s_g, codes, scales)
-             : launch_kernel(encode_t_kernel<uint16_t, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x,
+             : launch_kernel(encode_t_kernel<uint16_t, false>, grid, dim3(kTThreads), 0, stream, (const uint16_t*)x,
                              rows, cols, s_g, codes, scales);
 }
 
