@@ -267,7 +267,12 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
     const int qi = min(qbase + n, q_tokens - 1);
     const __bf16* qrow = q + ((int64_t)h * q_tokens + qi) * kAD;
 #pragma unroll
-    for (int s = 0; s < 8; s++) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+    for (int s = 0; s < 8; s++) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+      // opaque from here on: otherwise the compiler re-loads the queries
+      // from memory in every block and the first MFMAs wait for them
+      asm volatile("" : "+v"(qf[s]));
+    }
   }
 
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
