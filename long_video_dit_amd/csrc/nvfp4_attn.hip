@@ -286,17 +286,21 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
   if (blk0 + 1 < blk1) load_raw(raw, kc, ks, vc, vs, min((blk0 + 1) * kABN + t_dec, kv_tokens - 1), qd_dec);
   __syncthreads();
 
-  for (int blk = blk0; blk < blk1; blk++) {
-    const int buf = (blk - blk0) & 1;
-    attn_block(sm[buf], qf, oacc, m, l, c_k, kv_tokens - blk * kABN, lane);
-
-    // Next block: decode into the other LDS buffer (its last readers finished
-    // before the previous barrier), prefetch the one after.
+  // One block from `cur`; then the next block is decoded into `nxt` (its last
+  // readers finished before the previous barrier) and the one after is
+  // prefetched.  Unrolled by two so that each buffer is a compile-time LDS
+  // offset (the operand reads then need no per-block address arithmetic).
+  auto step = [&](int blk, AttnSmem& cur, AttnSmem& nxt) {
+    attn_block(cur, qf, oacc, m, l, c_k, kv_tokens - blk * kABN, lane);
     if (blk + 1 < blk1) {
-      decode_to_lds(raw, sm[buf ^ 1], t_dec, qd_dec);
+      decode_to_lds(raw, nxt, t_dec, qd_dec);
       if (blk + 2 < blk1) load_raw(raw, kc, ks, vc, vs, min((blk + 2) * kABN + t_dec, kv_tokens - 1), qd_dec);
     }
     __syncthreads();
+  };
+  for (int blk = blk0; blk < blk1; blk += 2) {
+    step(blk, sm[0], sm[1]);
+    if (blk + 1 < blk1) step(blk + 1, sm[1], sm[0]);
   }
 
   // l = this lane's partial sum + the other half's.
