@@ -150,7 +150,7 @@ nvfp4_status_t nvfp4_quantize_transposed(const void *x, int dtype, int64_t rows,
  * optimizations; this is its adaLN half, fused with the activation
  * quantization that follows it (the modulated activation never goes to HBM).
  * Two passes over x (amax, then encode), the amax partials kept in the codes
- * buffer.  Requires k % 16 == 0, 16 <= k <= 4096, rows_per_group >= 1,
+ * buffer.  Requires k % 16 == 0, 16 <= k <= 4096, rows < 2^33, rows_per_group >= 1,
  * 0 <= eps finite; shift and scale 16-byte aligned.  rows == 0 is allowed
  * (COMPUTE then writes s_g = 0).
  */

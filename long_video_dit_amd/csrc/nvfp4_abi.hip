@@ -116,7 +116,9 @@ nvfp4_status_t nvfp4_adaln_quantize(const void* x, int dtype, int64_t rows, int6
   if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_matrix(rows, k, true);
   if (st != NVFP4_OK) return st;
-  if (k > 4096 || rows_per_group <= 0 || !std::isfinite(eps) || !(eps >= 0.0f)) return NVFP4_ERR_SHAPE;
+  // one workgroup per 4 rows: the grid and the partial count stay below 2^31
+  if (k > 4096 || rows >= (int64_t(1) << 33) || rows_per_group <= 0 || !std::isfinite(eps) || !(eps >= 0.0f))
+    return NVFP4_ERR_SHAPE;
   if (!s_g || (rows > 0 && (!x || !codes || !scales || !shift || !scale))) return NVFP4_ERR_NULL;
   if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(shift, 16) ||
       !aligned(scale, 16))

@@ -137,6 +137,7 @@ def test_validation_errors_launch_nothing():
     assert ad(buf, 1, 4, 4112, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k > 4096
     assert ad(buf, 1, 4, 40, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # k % 16
     assert ad(buf, 1, 4, 64, buf, buf, 0, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # rows_per_group
+    assert ad(buf, 1, 1 << 33, 16, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # rows
     assert ad(buf, 1, 4, 64, buf, buf, 2, -1.0, buf, buf, buf, 0, None) == nv.ERR_SHAPE  # eps
     assert ad(buf, 1, 4, 64, buf, buf, 2, float("inf"), buf, buf, buf, 0, None) == nv.ERR_SHAPE
     assert ad(buf, 1, 4, 64, None, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_NULL
