@@ -3,9 +3,9 @@
 // Layout: a tensor is processed as G equal groups (G = 1 for a plain
 // tensor, G = heads for the KV cache), each group a flat run of elements
 // with its own fp32 scale.  Inside a group the work unit of one lane is 8
-// consecutive elements (16 B of bf16, 32 B of fp32); lanes 2j and 2j+1 own
-// one 16-element block and exchange their partial block maximum with one
-// cross-lane move.  All kernels are HBM-bound grid-stride loops.
+// consecutive elements (16 B of bf16, 32 B of fp32); in the amax pass lanes
+// 2j and 2j+1 share one 16-element block, and an encode lane owns two units,
+// a whole block.  All kernels are HBM-bound grid-stride loops.
 //
 //   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
@@ -149,12 +149,87 @@ __global__ void finalize_slot_kernel(float* __restrict__ s_g) {
   s_g[0] = __fdiv_rn(__uint_as_float(reinterpret_cast<const uint32_t*>(s_g)[0]), 2688.0f);
 }
 
-// grid: (X, G).  Each lane encodes 8-element units; the partner lane (lane ^ 1)
-// holds the other half of the 16-element block.  Group g reads units
-// [g * units_per_group, (g + 1) * units_per_group) of x and writes them at
-// unit g * out_group_stride + out_offset of the codes (and the matching scale
-// bytes): a plain tensor has out_group_stride = units_per_group and
-// out_offset = 0; a KV-cache append writes a slice of each head's rows.
+// One 8-element unit as loaded (16 B of bf16 or 32 B of fp32), converted to
+// fp32 only when it is encoded, so that the next units' loads can be issued
+// first.
+template <typename T>
+struct Raw8;
+
+template <>
+struct Raw8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int64_t unit) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + unit);
+  }
+  __device__ __forceinline__ void unpack(float (&f)[8]) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* __restrict__ x, int64_t unit) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(x) + 2 * unit;
+    a = __builtin_nontemporal_load(p);
+    b = __builtin_nontemporal_load(p + 1);
+  }
+  __device__ __forceinline__ void unpack(float (&f)[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+// The grid-stride loop of one lane over whole 16-element blocks b0,
+// b0 + stride, ... < nb of one group (units 2b and 2b + 1), so that the block
+// maximum needs no lane exchange and a lane stores 8 B of codes and its
+// block's scale byte.  The loads of the next block are issued before the
+// current one is encoded; their indexes are clamped to the last block
+// (always in bounds) and the stores need no predicate.
+template <typename T>
+__device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int64_t nb, int64_t b0, int64_t stride,
+                                                   const EncodeConsts& c, uint32_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, int64_t base) {
+  const int64_t last = nb - 1;
+  Raw8<T> nxt[2];
+  {
+    const int64_t bb = __builtin_elementwise_min(b0, last);
+    nxt[0].load(xg, 2 * bb);
+    nxt[1].load(xg, 2 * bb + 1);
+  }
+  for (int64_t bk = b0; bk < nb; bk += stride) {
+    const Raw8<T> cur[2] = {nxt[0], nxt[1]};
+    const int64_t bn = __builtin_elementwise_min(bk + stride, last);
+    nxt[0].load(xg, 2 * bn);
+    nxt[1].load(xg, 2 * bn + 1);
+    float f0[8], f1[8];
+    cur[0].unpack(f0);
+    cur[1].unpack(f1);
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(f0[i]), __builtin_fabsf(f1[i])));
+    const uint32_t sb = encode_scale(am, c);
+    const uint32_t w0 = encode8(f0, sb, c);
+    const uint32_t w1 = encode8(f1, sb, c);
+    __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(codes + base) + bk);
+    scales[(base >> 1) + bk] = (uint8_t)sb;
+  }
+}
+
+// grid: (X, G).  Each lane encodes whole 16-element blocks.  Group g reads
+// units [g * units_per_group, (g + 1) * units_per_group) of x and writes them
+// at unit g * out_group_stride + out_offset of the codes (and the matching
+// scale bytes): a plain tensor has out_group_stride = units_per_group and
+// out_offset = 0; a KV-cache append writes a slice of each head's rows.  Both
+// are even (whole blocks), so the 8-byte code stores stay aligned.  The
+// common case (an ordinary per-tensor scale) runs a copy of the loop in which
+// the encoder's mode is the constant 0, so that no mode test is left inside.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, int64_t units_per_group,
                                                           const float* __restrict__ s_g,
@@ -166,34 +241,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   const int64_t base = (int64_t)g * out_group_stride + out_offset;
   const T* xg = x + (int64_t)g * units_per_group * 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  constexpr int U = 2;
-  for (int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; u0 < units_per_group; u0 += U * stride) {
-    float f[U][8];
-    bool ok[U];
-#pragma unroll
-    for (int j = 0; j < U; j++) {
-      const int64_t u = u0 + j * stride;
-      ok[j] = u < units_per_group;  // uniform across the lane pair (units_per_group is even)
-      if (ok[j]) load8(xg, u, f[j]);
-      else {
-#pragma unroll
-        for (int i = 0; i < 8; i++) f[j][i] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < U; j++) {
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 1));
-      const uint32_t sb = encode_scale(am, c);
-      const uint32_t w = encode8(f[j], sb, c);
-      if (ok[j]) {
-        const int64_t u = u0 + j * stride;
-        codes[base + u] = w;
-        if ((threadIdx.x & 1) == 0) scales[(base + u) >> 1] = (uint8_t)sb;
-      }
-    }
+  const int64_t b0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t nb = units_per_group / 2;
+  if (c.mode == 0) {
+    EncodeConsts cf = c;
+    cf.mode = 0;
+    encode_lane_blocks(xg, nb, b0, stride, cf, codes, scales, base);
+  } else {
+    encode_lane_blocks(xg, nb, b0, stride, c, codes, scales, base);
   }
 }
 
