@@ -136,6 +136,25 @@ def test_quantize_config_tensors_full_size(cfg):
     assert np.array_equal(y, oracle.dequantize(o[0], o[1], o[2], "bf16"))
 
 
+@pytest.mark.parametrize("rows,k,where", [(2048, 8192, "last"), (2048, 8192, "slice3"), (4096, 8192, "first"),
+                                           (4096, 8192, "slice15")])
+def test_quantize_sliced_amax_outlier(rows, k, where):
+    """Tensors large enough for the amax pass to read them in slices (8 and 16 slices
+    of 2^18 units here): one outlier at the first or last element or at the first
+    element of a slice fixes s_g, and the whole result stays bit-exact."""
+    log("quantize sliced amax", rows, k, where)
+    gen = torch.Generator().manual_seed(rows + k)
+    x = torch.randn(rows, k, generator=gen)
+    flat = x.view(-1)
+    units = rows * k // 8
+    sub = 8 if units == 8 << 18 else 16
+    pos = {"last": flat.numel() - 1, "first": 0, "slice3": 3 * (units // sub) * 8,
+           "slice15": 15 * (units // sub) * 8}[where]
+    flat[pos] = -1000.0
+    g, o = _quant_both(x.to(torch.bfloat16), "sliced amax %dx%d %s" % (rows, k, where))
+    assert float(g[2].cpu()[0]) == float(np.float32(np.float32(1000.0) / np.float32(2688.0)))
+
+
 def test_quantize_deterministic():
     nv = _nv()
     a = workloads.activations(2).to(dev())
