@@ -5,7 +5,7 @@ The kernel computes y in fp32, so its y differs from the exact y by at most
   tau = 4 * (|1 + a| * (rstd * e_mu + |t| * e_r) + (|t (1 + a)| + |b|) * 2^-23),
   t = (x - mu) * rstd, e_mu = (k / 64 + 8) * 2^-24 * mean|x|, e_r = (k / 64 + 16) * 2^-24
 (the fp32 row sums: a sequential sum per lane over k / 64 values and a 6-level
-butterfly; then sqrt, division, the product and the fma, one rounding each).
+tree across the wave; then sqrt, division, the product and the fma, one rounding each).
 With the same s_g on both sides, a scale byte or a code may differ from the
 oracle's only where the exact block maximum or element lies within tau of the
 decision boundary between the two values; everything else must be identical,
