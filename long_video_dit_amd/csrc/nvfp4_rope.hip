@@ -18,8 +18,8 @@
 // Layout: one lane per 8-element unit of one token, looping over 4 heads
 // with that token's sines and cosines (they do not depend on the head); D / 8
 // divides 256, so in the grid-stride loop every thread keeps the same unit w
-// of head_dim and its four th_i are computed once.  Lanes 2j and 2j + 1 hold
-// one 16-element block.
+// of head_dim and reads its four th_i once from the workgroup's table.  Lanes
+// 2j and 2j + 1 hold one 16-element block.
 #include <hip/hip_runtime.h>
 
 #include "nvfp4_device.h"
