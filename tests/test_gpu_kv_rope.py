@@ -60,7 +60,8 @@ def _run(H, Tc, Tn, D, off, positions, base, seed, label):
 
 @pytest.mark.parametrize("H,Tc,Tn,D,off,explicit,base", [
     (2, 256, 64, 128, 100, False, 10000.0), (3, 300, 37, 64, 0, True, 10000.0), (1, 64, 64, 16, 0, False, 500.0),
-    (2, 512, 200, 256, 311, True, 10000.0), (1, 80, 1, 128, 79, False, 10000.0)])
+    (2, 512, 200, 256, 311, True, 10000.0), (1, 80, 1, 128, 79, False, 10000.0),
+    (1, 16, 5, 2048, 3, False, 10000.0), (2, 40, 33, 32, 1, True, 10000.0)])  # largest head_dim; 32
 def test_rope_append(H, Tc, Tn, D, off, explicit, base):
     log("rope append", H, Tc, Tn, D, off, explicit, base)
     positions = None
