@@ -54,7 +54,9 @@ hipError_t launch_kv_rope_append(const void* k_new, int64_t heads, int64_t token
 // bits into it, round in place (three kernels, no scratch).
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream);
 // Encode pass; group g is written at unit g * out_group_stride + out_offset
-// (out_group_stride < 0: = units_per_group, a dense tensor).
+// (out_group_stride < 0: = units_per_group, a dense tensor).  units_per_group,
+// out_group_stride and out_offset must be even (whole 16-element blocks), else
+// hipErrorInvalidValue.
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
                          uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride = -1,
                          int64_t out_offset = 0);

@@ -475,6 +475,8 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
                          int64_t out_offset) {
   if (units_per_group == 0) return hipSuccess;
   if (out_group_stride < 0) out_group_stride = units_per_group;
+  // whole blocks: the kernel stores 8 bytes of codes per block
+  if ((units_per_group | out_group_stride | out_offset) & 1) return hipErrorInvalidValue;
   const int cus = device_cu_count();
   const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 16 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
