@@ -478,7 +478,9 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
   // whole blocks: the kernel stores 8 bytes of codes per block
   if ((units_per_group | out_group_stride | out_offset) & 1) return hipErrorInvalidValue;
   const int cus = device_cu_count();
-  const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 16 / groups));
+  // up to 64 workgroups per CU (a few blocks per thread): measured 6% faster
+  // on the KV tensor than 16 per CU, and slower again at 128
+  const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 64 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (dtype == kDtypeF32)
     return launch_kernel(encode_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group, s_g,
@@ -509,7 +511,8 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
   if (blocks_per_group == 0) return hipSuccess;
   const int64_t units = 2 * blocks_per_group;
   const int cus = device_cu_count();
-  const int bx = grid_blocks(units, 2, std::max(1, cus * 16 / groups));
+  // up to 128 workgroups per CU: 92 against 105 us on one KV tensor with 16
+  const int bx = grid_blocks(units, 2, std::max(1, cus * 128 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (y_dtype == kDtypeF32)
     return launch_kernel(dequant_kernel<false>, grid, dim3(kThreads), 0, stream, (const uint32_t*)codes, scales, units,
