@@ -478,9 +478,10 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
   // whole blocks: the kernel stores 8 bytes of codes per block
   if ((units_per_group | out_group_stride | out_offset) & 1) return hipErrorInvalidValue;
   const int cus = device_cu_count();
-  // up to 64 workgroups per CU (a few blocks per thread): measured 6% faster
-  // on the KV tensor than 16 per CU, and slower again at 128
-  const int bx = grid_blocks(units_per_group, 2, std::max(1, cus * 64 / groups));
+  // about three blocks per thread, up to 64 workgroups per CU: on a KV tensor
+  // 6% faster than 16 per CU (and slower again at 128); on [16384, 3072] one
+  // block per thread was slower than three
+  const int bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (dtype == kDtypeF32)
     return launch_kernel(encode_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group, s_g,
@@ -511,8 +512,9 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
   if (blocks_per_group == 0) return hipSuccess;
   const int64_t units = 2 * blocks_per_group;
   const int cus = device_cu_count();
-  // up to 128 workgroups per CU: 92 against 105 us on one KV tensor with 16
-  const int bx = grid_blocks(units, 2, std::max(1, cus * 128 / groups));
+  // about three units per thread, up to 128 workgroups per CU: 92 against
+  // 105 us on one KV tensor with 16 per CU
+  const int bx = grid_blocks(units, 3, std::max(1, cus * 128 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
   if (y_dtype == kDtypeF32)
     return launch_kernel(dequant_kernel<false>, grid, dim3(kThreads), 0, stream, (const uint32_t*)codes, scales, units,
