@@ -159,17 +159,16 @@ __device__ __forceinline__ f16x8 v_frag(const AttnSmem& sm, int dt, int tau, int
 // the same values the second product uses.
 __device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], float c, int valid, int hh, float& m, float& l,
                                               f16x8 (&pf)[4]) {
-  // block maximum of c * s (c >= 0: c * max s, else c * min s)
+  // block maximum of c * s (c >= 0: a negative factor is folded into the
+  // queries); the two halves of the wave exchange theirs with one lane swap
   float bm = s[0][0];
-  if (c >= 0.0f) {
 #pragma unroll
-    for (int i = 1; i < 32; i++) bm = fmaxf(bm, s[i >> 4][i & 15]);
-  } else {
-#pragma unroll
-    for (int i = 1; i < 32; i++) bm = fminf(bm, s[i >> 4][i & 15]);
-  }
+  for (int i = 1; i < 32; i++) bm = fmaxf(bm, s[i >> 4][i & 15]);
   bm *= c;
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   // Lazy maximum: the reference point only moves when the block maximum
   // exceeds it by more than 2^8, so probabilities stay <= 256 (fp16 keeps its
   // 2^-11 relative rounding there) and the output rescale is rare.
@@ -257,7 +256,10 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
   const uint8_t* ks = k_scales + cache_row0 * (kAD / 16);
   const uint8_t* vc = v_codes + cache_row0 * (kAD / 2);
   const uint8_t* vs = v_scales + cache_row0 * (kAD / 16);
-  const float c_k = scale * k_hs[h] * kLog2e;  // raw dot product -> log2 units
+  const float c_raw = scale * k_hs[h] * kLog2e;  // raw dot product -> log2 units
+  // a negative factor is folded into the queries (exact bf16 negation)
+  const float c_k = __builtin_fabsf(c_raw);
+  const uint32_t qsign = c_raw < 0.0f ? 0x80008000u : 0u;
   const float s_gv = v_hs[h];
 
   // Queries of this wave (one column tile of 32); rows past q_tokens repeat the last row.
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(kAW * 64, 1) void attn_nvfp4_kv_kernel(
     const __bf16* qrow = q + ((int64_t)h * q_tokens + qi) * kAD;
 #pragma unroll
     for (int s = 0; s < 8; s++) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh) ^ qsign);
       // opaque from here on: otherwise the compiler re-loads the queries
       // from memory in every block and the first MFMAs wait for them
       asm volatile("" : "+v"(qf[s]));
