@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void adaln_encode_kernel(const T* 
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(y[i]));
-    am = __builtin_fmaxf(am, __shfl_xor(am, 1));  // the other half of the block (units is even)
+    am = pair_max(am);  // the other half of the block (units is even)
     const uint32_t sb = encode_scale(am, c);
     const uint32_t w = encode8(y, sb, c);
     if (u < units) {

@@ -87,6 +87,12 @@ __device__ __noinline__ uint32_t code_resolve(float x, float sb_val, float s_g, 
   return ((__float_as_uint(x) >> 31) << 3) | m;
 }
 
+// max(v, v of lane ^ 1): the block maximum of a lane pair, with one DPP move
+// (quad_perm [1, 0, 3, 2]) instead of an LDS permute.
+__device__ __forceinline__ float pair_max(float v) {
+  return __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+}
+
 // Two fp32 -> one byte of two E2M1 codes (first value in the low nibble),
 // written into byte `sel` of `old`.  Scale 1.0: plain RNE with saturation.
 #define NVFP4_PK_FP4(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))

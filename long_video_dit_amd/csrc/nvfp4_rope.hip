@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_encode_kernel(
       float am = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(y[i]));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 1));
+      am = pair_max(am);
       const uint32_t sb = encode_scale(am, c);
       const int64_t row = (int64_t)h * cache_tokens + token_offset;  // this head's first appended row
       codes[row * upt + u] = encode8(y, sb, c);
