@@ -71,6 +71,13 @@ def test_attention_peaked_softmax():
     _run(2, 300, 2048, 2000, seed=3, qscale=6.0)
 
 
+def test_attention_negative_and_zero_scale():
+    """A negative softmax factor (folded into the queries' signs by the kernel)
+    and a zero one (every weight equal: the plain mean of the values)."""
+    _run(2, 100, 300, 250, seed=5, scale=-0.2)
+    _run(1, 64, 200, 200, seed=6, scale=0.0)
+
+
 def test_attention_full_cache_sampled_queries():
     """The 24-head 65,536-token cache, 1,024 queries per head; sampled query rows."""
     _run(24, 1024, 65536, 65536, seed=11, q_idx=np.array([0, 1, 255, 256, 511, 777, 1023]))
