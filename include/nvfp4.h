@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 typedef enum {
   NVFP4_OK = 0,
@@ -74,7 +74,7 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
 int nvfp4_abi_version(void);
 
 /* Static, NUL-terminated description of a status code. */
-const char *nvfp4_status_string(int status);
+const char *nvfp4_status_string(nvfp4_status_t status);
 
 /*
  * Per-tensor scale alone: s_g[0] = RN_f32(max |x| / (6 * 448)) for x
@@ -90,7 +90,7 @@ const char *nvfp4_status_string(int status);
  * the call has finished on `stream`.  rows == 0 gives s_g = 0.  Requires
  * k > 0, k % 16 == 0, rows * k < 2^40.
  */
-nvfp4_status_t nvfp4_global_scale(const void *x, int dtype, int64_t rows, int64_t k, float *s_g,
+nvfp4_status_t nvfp4_global_scale(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, float *s_g,
                                   void *stream);
 
 /*
@@ -103,7 +103,7 @@ nvfp4_status_t nvfp4_global_scale(const void *x, int dtype, int64_t rows, int64_
  * the codes buffer serves as scratch for the amax partials before it is
  * overwritten.  Requires k > 0, k % 16 == 0, rows * k < 2^40.
  */
-nvfp4_status_t nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes,
+nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, uint8_t *codes,
                               uint8_t *scales, float *s_g, int flags, void *stream);
 
 /*
@@ -127,7 +127,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, int dtype, int64_t rows, int64_t k,
  * the codes buffer serves as scratch for the amax partials.  Requires
  * rows > 0, rows % 16 == 0, rows * cols < 2^40.
  */
-nvfp4_status_t nvfp4_quantize_transposed(const void *x, int dtype, int64_t rows, int64_t cols,
+nvfp4_status_t nvfp4_quantize_transposed(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
                                          uint8_t *codes_t, uint8_t *scales_t, float *s_g, int flags,
                                          void *stream);
 
@@ -154,7 +154,7 @@ nvfp4_status_t nvfp4_quantize_transposed(const void *x, int dtype, int64_t rows,
  * 0 <= eps finite; shift and scale 16-byte aligned.  rows == 0 is allowed
  * (COMPUTE then writes s_g = 0).
  */
-nvfp4_status_t nvfp4_adaln_quantize(const void *x, int dtype, int64_t rows, int64_t k, const float *shift,
+nvfp4_status_t nvfp4_adaln_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, const float *shift,
                                     const float *scale, int64_t rows_per_group, float eps, uint8_t *codes,
                                     uint8_t *scales, float *s_g, int flags, void *stream);
 
@@ -166,7 +166,7 @@ nvfp4_status_t nvfp4_adaln_quantize(const void *x, int dtype, int64_t rows, int6
  * dequantization).
  */
 nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *s_g,
-                                int64_t rows, int64_t k, void *y, int y_dtype, void *stream);
+                                int64_t rows, int64_t k, void *y, nvfp4_dtype_t y_dtype, void *stream);
 
 /*
  * W4A4 GEMM, the nn.Linear convention C = A . B^T:
@@ -182,20 +182,27 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, con
  */
 nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sg,
                           const uint8_t *b_codes, const uint8_t *b_scales, const float *b_sg,
-                          int64_t M, int64_t N, int64_t K, void *c, int c_dtype, void *stream);
+                          int64_t M, int64_t N, int64_t K, void *c, nvfp4_dtype_t c_dtype, void *stream);
 
 /*
- * Activation-quantizing linear: quantize A (a_dtype F32 or BF16, [M][K])
- * with a per-tensor scale computed from the data, then C = A_q . B^T as in
- * nvfp4_gemm.  a_sg [1], a_codes [M][K/2] and a_scales [M][K/16] are outputs
- * owned by the caller (the packed activation, bit-identical to
- * nvfp4_quantize's); the GEMM reads them back from L2/MALL.  One call
- * enqueues amax, finalize, encode and GEMM kernels on `stream`.
+ * Activation-quantizing linear: quantize A (a_dtype F32 or BF16, [M][K]) to
+ * NVFP4, then C = A_q . B^T as in nvfp4_gemm.
+ *   flags NVFP4_SCALE_COMPUTE: a_sg [1] is an output, RN_f32(max |A| / 2688);
+ *   flags NVFP4_SCALE_GIVEN:   a_sg [1] is an input, e.g. written earlier on the
+ *         stream by nvfp4_global_scale (the scale never leaves the device);
+ *   a_codes [M][K/2], a_scales [M][K/16]: the packed activation, outputs,
+ *         bit-identical to nvfp4_quantize with the same flags and a_sg.
+ * The packed activation is required, not optional: the GEMM reads it back (from
+ * L2 / MALL) and the library allocates nothing, so the caller owns that memory.
+ * One call enqueues, on `stream`, amax and finalize kernels (COMPUTE only), the
+ * encode kernel and the GEMM.  Per the arXiv abstract (W4A4 NVFP4 linears) and
+ * the yourai.pro page (reduced KV-cache synchronization: scales stay on the
+ * device).  Shape rules of nvfp4_gemm; unknown flags give NVFP4_ERR_FLAGS.
  */
-nvfp4_status_t nvfp4_gemm_fused_act(const void *a, int a_dtype, int64_t M, int64_t K, float *a_sg,
+nvfp4_status_t nvfp4_gemm_fused_act(const void *a, nvfp4_dtype_t a_dtype, int64_t M, int64_t K, float *a_sg,
                                     uint8_t *a_codes, uint8_t *a_scales, const uint8_t *b_codes,
                                     const uint8_t *b_scales, const float *b_sg, int64_t N, void *c,
-                                    int c_dtype, void *stream);
+                                    nvfp4_dtype_t c_dtype, int flags, void *stream);
 
 /*
  * NVFP4 KV cache quantize: kv [heads][tokens][head_dim] bf16 ->

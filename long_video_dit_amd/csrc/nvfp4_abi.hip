@@ -53,7 +53,7 @@ extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
-const char* nvfp4_status_string(int status) {
+const char* nvfp4_status_string(nvfp4_status_t status) {
   switch (status) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
@@ -66,7 +66,7 @@ const char* nvfp4_status_string(int status) {
   }
 }
 
-nvfp4_status_t nvfp4_global_scale(const void* x, int dtype, int64_t rows, int64_t k, float* s_g, void* stream) {
+nvfp4_status_t nvfp4_global_scale(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, float* s_g, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
   nvfp4_status_t st = check_matrix(rows, k, true);
   if (st != NVFP4_OK) return st;
@@ -75,7 +75,7 @@ nvfp4_status_t nvfp4_global_scale(const void* x, int dtype, int64_t rows, int64_
   return from_hip(nvfp4::launch_global_scale_slot(x, dtype, rows * k / 8, s_g, (hipStream_t)stream));
 }
 
-nvfp4_status_t nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
+nvfp4_status_t nvfp4_quantize(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
                               float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
   if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
@@ -92,7 +92,7 @@ nvfp4_status_t nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t k,
   return from_hip(nvfp4::launch_encode(x, dtype, units, 1, s_g, reinterpret_cast<uint32_t*>(codes), scales, s));
 }
 
-nvfp4_status_t nvfp4_quantize_transposed(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes_t,
+nvfp4_status_t nvfp4_quantize_transposed(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols, uint8_t* codes_t,
                                          uint8_t* scales_t, float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
   if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
@@ -109,7 +109,7 @@ nvfp4_status_t nvfp4_quantize_transposed(const void* x, int dtype, int64_t rows,
   return from_hip(nvfp4::launch_encode_t(x, dtype, rows, cols, s_g, reinterpret_cast<uint32_t*>(codes_t), scales_t, s));
 }
 
-nvfp4_status_t nvfp4_adaln_quantize(const void* x, int dtype, int64_t rows, int64_t k, const float* shift,
+nvfp4_status_t nvfp4_adaln_quantize(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, const float* shift,
                                     const float* scale, int64_t rows_per_group, float eps, uint8_t* codes,
                                     uint8_t* scales, float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
@@ -128,7 +128,7 @@ nvfp4_status_t nvfp4_adaln_quantize(const void* x, int dtype, int64_t rows, int6
 }
 
 nvfp4_status_t nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t rows,
-                                int64_t k, void* y, int y_dtype, void* stream) {
+                                int64_t k, void* y, nvfp4_dtype_t y_dtype, void* stream) {
   if (!valid_dtype(y_dtype)) return NVFP4_ERR_DTYPE;
   nvfp4_status_t st = check_matrix(rows, k, true);
   if (st != NVFP4_OK) return st;
@@ -156,25 +156,30 @@ static nvfp4_status_t check_gemm(const uint8_t* a_codes, const uint8_t* a_scales
 
 nvfp4_status_t nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_sg, const uint8_t* b_codes,
                           const uint8_t* b_scales, const float* b_sg, int64_t M, int64_t N, int64_t K, void* c,
-                          int c_dtype, void* stream) {
+                          nvfp4_dtype_t c_dtype, void* stream) {
   nvfp4_status_t st = check_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype);
   if (st != NVFP4_OK) return st;
   return from_hip(nvfp4::launch_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype,
                                      (hipStream_t)stream));
 }
 
-nvfp4_status_t nvfp4_gemm_fused_act(const void* a, int a_dtype, int64_t M, int64_t K, float* a_sg, uint8_t* a_codes,
-                                    uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
-                                    const float* b_sg, int64_t N, void* c, int c_dtype, void* stream) {
+nvfp4_status_t nvfp4_gemm_fused_act(const void* a, nvfp4_dtype_t a_dtype, int64_t M, int64_t K, float* a_sg,
+                                    uint8_t* a_codes, uint8_t* a_scales, const uint8_t* b_codes,
+                                    const uint8_t* b_scales, const float* b_sg, int64_t N, void* c,
+                                    nvfp4_dtype_t c_dtype, int flags, void* stream) {
   if (!valid_dtype(a_dtype)) return NVFP4_ERR_DTYPE;
+  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype);
   if (st != NVFP4_OK) return st;
   if (!a) return NVFP4_ERR_NULL;
   if (!aligned(a, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const int64_t units = M * K / 8;
-  st = from_hip(nvfp4::launch_global_scale(a, a_dtype, units, 1, reinterpret_cast<uint32_t*>(a_codes), units, a_sg, s));
-  if (st != NVFP4_OK) return st;
+  if (flags == NVFP4_SCALE_COMPUTE) {
+    st = from_hip(
+        nvfp4::launch_global_scale(a, a_dtype, units, 1, reinterpret_cast<uint32_t*>(a_codes), units, a_sg, s));
+    if (st != NVFP4_OK) return st;
+  }
   st = from_hip(nvfp4::launch_encode(a, a_dtype, units, 1, a_sg, reinterpret_cast<uint32_t*>(a_codes), a_scales, s));
   if (st != NVFP4_OK) return st;
   return from_hip(nvfp4::launch_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype, s));
@@ -259,11 +264,10 @@ nvfp4_status_t kv_attention_workspace_size(int64_t heads, int64_t q_tokens, int6
   return NVFP4_OK;
 }
 
-nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim, const uint8_t* k_codes,
-                            const uint8_t* k_scales, const float* k_head_scales, const uint8_t* v_codes,
-                            const uint8_t* v_scales, const float* v_head_scales, int64_t cache_tokens,
-                            int64_t kv_tokens, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+static nvfp4_status_t check_attention(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim,
+                                      const uint8_t* k_codes, const uint8_t* k_scales, const float* k_head_scales,
+                                      const uint8_t* v_codes, const uint8_t* v_scales, const float* v_head_scales,
+                                      int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, const void* out) {
   if (head_dim != 128 || heads <= 0 || heads > 65535 || q_tokens < 0 || q_tokens >= (int64_t(1) << 31) ||
       kv_tokens <= 0 || kv_tokens > cache_tokens || cache_tokens >= (int64_t(1) << 31) ||
       heads > kMaxElems / (cache_tokens * head_dim) || (q_tokens > 0 && heads > kMaxElems / (q_tokens * head_dim)) ||
@@ -273,9 +277,20 @@ nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int6
       (q_tokens > 0 && (!q || !out)))
     return NVFP4_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
-      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(k_head_scales, 4) || !aligned(v_head_scales, 4) ||
-      !aligned(workspace, 16))
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(k_head_scales, 4) || !aligned(v_head_scales, 4))
     return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim, const uint8_t* k_codes,
+                            const uint8_t* k_scales, const float* k_head_scales, const uint8_t* v_codes,
+                            const uint8_t* v_scales, const float* v_head_scales, int64_t cache_tokens,
+                            int64_t kv_tokens, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  nvfp4_status_t st = check_attention(q, heads, q_tokens, head_dim, k_codes, k_scales, k_head_scales, v_codes,
+                                      v_scales, v_head_scales, cache_tokens, kv_tokens, softmax_scale, out);
+  if (st != NVFP4_OK) return st;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
   const int64_t ws = workspace ? (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX) : 0;
   return from_hip(nvfp4::launch_kv_attention(q, k_codes, k_scales, k_head_scales, v_codes, v_scales, v_head_scales,
                                              heads, q_tokens, cache_tokens, kv_tokens, softmax_scale, out, workspace,

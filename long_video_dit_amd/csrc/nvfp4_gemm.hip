@@ -14,14 +14,23 @@
 // elements, which cannot represent E4M3 scales per 16 exactly, so it is not
 // used.
 //
-// Tiling.  256 x 256 output tile per 256-thread workgroup (4 waves in 2 x 2,
-// 128 x 128 per wave = 4 x 4 MFMA tiles of 32 x 32), K in chunks of 128,
-// double-buffered LDS (72 KB).  Within a chunk the K order is permuted the
-// same way for A and B: lane half h of k16-step t of sub-chunk s carries
+// Two kernels share that decode and MFMA code.  Both take a 256 x 256 output
+// tile per 256-thread workgroup (4 waves in 2 x 2, 128 x 128 per wave = 4 x 4
+// MFMA tiles of 32 x 32); within a stage the K order is permuted the same way
+// for A and B: lane half h of k16-step t of sub-chunk s carries
 // k = 64 s + 32 h + 8 t + (0..7), so every lane reads its 32 codes of a
-// sub-chunk with one 16-byte LDS read.  Workgroup ids are remapped so that
-// consecutive tiles land on the same XCD (ids are dealt round-robin over the
-// 8 XCDs), then grouped 8 tile-rows high for L2 reuse.
+// sub-chunk with one 16-byte LDS read.
+//   gemm_w4a4_fast_kernel (K % 512 == 0, aligned operands): persistent, one
+//     workgroup per CU walking its tiles; stages of K = 256 copied global ->
+//     LDS by the DMA path (global_load_lds_dwordx4), two stages plus a 16 KB
+//     epilogue buffer in the 160 KB of LDS; hand-interleaved MFMA / decode
+//     steps.
+//   gemm_w4a4_kernel (any K % 16 == 0, any alignment): one tile per
+//     workgroup, register-staged stages of K = 128, double-buffered LDS
+//     (72 KB), zero-filled K tails.
+// Workgroup ids (fast kernel: tile indices) are remapped so that consecutive
+// tiles land on the same XCD (ids are dealt round-robin over the 8 XCDs),
+// then grouped 8 tile-rows high for L2 reuse.
 #include <hip/hip_runtime.h>
 #include <type_traits>
 

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
                                                             const float* __restrict__ s_g,
                                                             uint32_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
-  // Staging: codes [64 columns][32 words + 2 pad], scales [64 columns][16 B].
+  // Staging: codes [kTC = 128 columns][32 words + 2 pad], scales [128 columns][16 B].
   __shared__ uint32_t sc[kTC][34];
   __shared__ uint32_t ss[kTC][4];
   const EncodeConsts c = make_encode_consts(s_g[0]);

@@ -68,7 +68,7 @@ def _load():
         "orc_adaln": (c_i, [c_p, c_i, c_i64, c_i64, c_p, c_p, c_i64, c_d, c_p]),
         "orc_kv_dequantize": (c_i, [c_p, c_p, c_p, c_i64, c_i64, c_i64, c_p]),
         "orc_kv_attention": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_d,
-                                   c_p, c_i64, c_p, c_p]),
+                                   c_p, c_i64, c_p, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,13 +275,14 @@ def kv_dequantize(codes, scales, head_scales):
     return out
 
 
-def kv_attention(q, k_cache, v_cache, kv_tokens, scale, q_idx=None):
+def kv_attention(q, k_cache, v_cache, kv_tokens, scale, q_idx=None, return_norm=False):
     """Softmax attention of bf16 queries q (uint16 bits [H, Tq, D]) over the first
     kv_tokens rows of the NVFP4 caches k_cache, v_cache = (codes [H, T, D/2],
     scales [H, T, D/16], head_scales [H]); fp64 on the exact dequantized rows.
 
     Returns (out, wabs), float64 [H, nq, D]: the attention output and
-    sum_j w_j |v_j| / sum_j w_j (q_idx selects the queries of every head)."""
+    sum_j w_j |v_j| / sum_j w_j (q_idx selects the queries of every head); with
+    return_norm also the softmax normaliser sum_j w_j [H, nq] (w_j = exp(s_j - max s))."""
     q = np.ascontiguousarray(q)
     if q.dtype != np.uint16 or q.ndim != 3:
         raise OracleError("kv_attention expects uint16 bf16 bits [H, Tq, D]")
@@ -295,7 +296,8 @@ def kv_attention(q, k_cache, v_cache, kv_tokens, scale, q_idx=None):
     nq = Tq if qi is None else qi.size
     out = np.zeros((H, nq, D), np.float64)
     wabs = np.zeros((H, nq, D), np.float64)
+    lsum = np.zeros((H, nq), np.float64)
     _check(_load().orc_kv_attention(_ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kh), _ptr(vc), _ptr(vs), _ptr(vh),
                                     T, kv_tokens, float(scale), None if qi is None else _ptr(qi), nq,
-                                    _ptr(out), _ptr(wabs)))
-    return out, wabs
+                                    _ptr(out), _ptr(wabs), _ptr(lsum)))
+    return (out, wabs, lsum) if return_norm else (out, wabs)

@@ -389,15 +389,17 @@ static void decode_kv_row(const uint8_t *codes, const uint8_t *scales, float s_g
  *   s_j = scale * sum_d q[i][d] k[j][d],  w_j = exp(s_j - max_j s_j),
  *   out[i][d]  = sum_j w_j v[j][d] / sum_j w_j,
  *   wabs[i][d] = sum_j w_j |v[j][d]| / sum_j w_j,
+ *   lsum[i]    = sum_j w_j  (the softmax normaliser, >= 1),
  * with k, v the exact dequantized rows; fp64 throughout, token order.  The
  * cache is [heads][cache_tokens][...]; q and the outputs [heads][q_tokens or
- * n_q][head_dim].  q_idx (n_q entries) restricts the queries of every head;
- * NULL computes all q_tokens. */
+ * n_q][head_dim] (lsum [heads][q_tokens or n_q], optional: NULL skips it).
+ * q_idx (n_q entries) restricts the queries of every head; NULL computes all
+ * q_tokens. */
 int orc_kv_attention(const uint16_t *q, int64_t heads, int64_t q_tokens, int64_t head_dim,
                      const uint8_t *k_codes, const uint8_t *k_scales, const float *k_hs,
                      const uint8_t *v_codes, const uint8_t *v_scales, const float *v_hs,
                      int64_t cache_tokens, int64_t kv_tokens, double scale, const int64_t *q_idx,
-                     int64_t n_q, double *out, double *wabs) {
+                     int64_t n_q, double *out, double *wabs, double *lsum) {
   if (heads <= 0 || q_tokens < 0 || head_dim <= 0 || head_dim % 16 != 0 || kv_tokens <= 0 ||
       kv_tokens > cache_tokens || !isfinite(scale))
     return ORC_ERR_SHAPE;
@@ -456,6 +458,7 @@ int orc_kv_attention(const uint16_t *q, int64_t heads, int64_t q_tokens, int64_t
           o[d] /= l;
           wa[d] /= l;
         }
+        if (lsum) lsum[h * nq + ii] = l;
       }
       free(s);
       free(qd);

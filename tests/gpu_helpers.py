@@ -123,3 +123,35 @@ def check_quant_near_exact(codes, scales, y, tau, s_g, label):
     n_diff = len(diff) + 16 * len(bad_b)
     log(label, "elements off the exact rounding: %d of %d (%d blocks)" % (len(diff), y.size, len(bad_b)))
     assert n_diff <= 1e-4 * y.size + 16
+
+
+def window_sample(n, window=64, seed=0):
+    """One index in every `window`-wide window of 0 .. n-1 (the last one ragged), at offsets
+    that run through every residue mod 32, plus 0 and n - 1.  Any output tile of the GEMM that is
+    at least 2 windows wide therefore holds at least two sampled indices."""
+    idx = [0, n - 1]
+    for i, w0 in enumerate(range(0, n, window)):
+        width = min(window, n - w0)
+        idx.append(w0 + (17 * i + 5 + seed) % width)
+    return np.unique(np.asarray(idx, np.int64))
+
+
+def check_gemm_tiles(c, ao, bo, bf16_out, label, seed=0, tile=256):
+    """GEMM output c (float64 [M, N]) against the oracle on the cross product of sampled rows and
+    columns (window_sample of both) plus whole rows 0, M-1 and columns 0, N-1; asserts that every
+    tile x tile output tile has at least 4 compared elements.  Returns the worst err / bound."""
+    M, N = c.shape
+    rows, cols = window_sample(M, seed=seed), window_sample(N, seed=seed + 3)
+    cover = np.zeros(((M + tile - 1) // tile, (N + tile - 1) // tile), np.int64)
+    np.add.at(cover, (rows[:, None] // tile, cols[None, :] // tile), 1)
+    assert cover.min() >= 4, "%s: a %dx%d tile has only %d sampled outputs" % (label, tile, tile, cover.min())
+    ref, tot = oracle.gemm_ref(*ao, *bo, rows=rows, cols=cols)
+    w = check_gemm_bound(c[np.ix_(rows, cols)], ref, tot, bf16_out, label + " tiles")
+    edge_r, edge_c = np.array([0, M - 1]), np.array([0, N - 1])
+    ref, tot = oracle.gemm_ref(*ao, *bo, rows=edge_r)
+    w = max(w, check_gemm_bound(c[edge_r], ref, tot, bf16_out, label + " rows"))
+    ref, tot = oracle.gemm_ref(*ao, *bo, cols=edge_c)
+    w = max(w, check_gemm_bound(c[:, edge_c], ref, tot, bf16_out, label + " cols"))
+    log(label, "compared %d x %d sampled outputs (every %dx%d tile >= %d) + edges, worst err/bound %.3g" % (
+        rows.size, cols.size, tile, tile, cover.min(), w))
+    return w

@@ -43,7 +43,7 @@ def test_binding_signatures_cover_header():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_abi_version() == 2
     for st in range(7):
         assert len(lib.nvfp4_status_string(st)) >= 2
     assert lib.nvfp4_status_string(99) == b"unknown status"
@@ -86,9 +86,15 @@ def test_validation_errors_launch_nothing():
     assert lib.nvfp4_gemm(buf, None, buf, buf, buf, buf, 8, 8, 32, buf, 1, None) == nv.ERR_NULL
     assert lib.nvfp4_gemm(buf, buf, buf, odd, buf, buf, 8, 8, 32, buf, 1, None) == nv.ERR_ALIGN
     # fused activation linear
-    assert lib.nvfp4_gemm_fused_act(buf, 5, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_DTYPE
-    assert lib.nvfp4_gemm_fused_act(None, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_NULL
-    assert lib.nvfp4_gemm_fused_act(buf, 1, 8, 48 + 8, buf, buf, buf, buf, buf, buf, 8, buf, 1, None) == nv.ERR_SHAPE
+    fa = lib.nvfp4_gemm_fused_act
+    assert fa(buf, 5, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_DTYPE
+    assert fa(buf, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 7, 0, None) == nv.ERR_DTYPE  # c dtype
+    assert fa(buf, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 2, None) == nv.ERR_FLAGS
+    assert fa(None, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_NULL
+    assert fa(buf, 1, 8, 32, None, buf, buf, buf, buf, buf, 8, buf, 1, 1, None) == nv.ERR_NULL  # a_sg, given
+    assert fa(buf, 1, 8, 32, buf, None, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_NULL  # a_codes
+    assert fa(buf, 1, 8, 48 + 8, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_SHAPE
+    assert fa(odd, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_ALIGN
     # KV cache
     assert lib.kv_quantize(buf, 0, 16, 128, buf, buf, buf, None) == nv.ERR_SHAPE
     assert lib.kv_quantize(buf, 4, 16, 120, buf, buf, buf, None) == nv.ERR_SHAPE
@@ -192,3 +198,59 @@ def test_gemm_fast_path_leaves_m0_to_the_lds_copies():
                 inside = False
             elif not inside:
                 assert not re.search(r"\bm0\b", line.split(";")[0]), (k, line)
+
+
+def test_binding_rejects_mismatched_operands():
+    """The binding checks every operand's shape and dtype against the sizes it
+    derives and raises ValueError before any call into the library (CPU
+    tensors here: the shape check comes first, the device check last)."""
+    import torch
+    from long_video_dit_amd import nvfp4 as nv
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    q = lambda r, k: (u8(r, k // 2), u8(r, k // 16), f32(1))
+    cases = [
+        ("codes", lambda: nv.quantize(bf(8, 64), out=(u8(8, 16), u8(8, 4)))),
+        ("scales", lambda: nv.quantize(bf(8, 64), out=(u8(8, 32), u8(8, 5)))),
+        ("s_g", lambda: nv.quantize(bf(8, 64), s_g=f32(2))),
+        ("dtype", lambda: nv.quantize(torch.zeros(8, 64, dtype=torch.float16))),
+        ("multiple of 16", lambda: nv.quantize(bf(8, 40))),
+        ("codes", lambda: nv.quantize_transposed(bf(32, 8), out=(u8(32, 16), u8(8, 2)))),
+        ("K", lambda: nv.gemm(q(8, 64), q(4, 32))),
+        ("b scales", lambda: nv.gemm(q(8, 64), (u8(4, 32), u8(4, 3), f32(1)))),
+        ("a s_g", lambda: nv.gemm((u8(8, 32), u8(8, 4), f32(3)), q(4, 64))),
+        ("out", lambda: nv.gemm(q(8, 64), q(4, 64), out=f32(4, 8))),
+        ("out", lambda: nv.gemm(q(8, 64), q(4, 64), out=torch.zeros(8, 4, dtype=torch.float16))),
+        ("K", lambda: nv.gemm_fused_act(bf(8, 64), q(4, 128))),
+        ("a_q codes", lambda: nv.gemm_fused_act(bf(8, 64), q(4, 64), a_q=(u8(8, 31), u8(8, 4)))),
+        ("s_g", lambda: nv.gemm_fused_act(bf(8, 64), q(4, 64), s_g=f32(1, 2))),
+        ("scales", lambda: nv.dequantize(u8(8, 32), u8(8, 3), f32(1))),
+        ("out", lambda: nv.dequantize(u8(8, 32), u8(8, 4), f32(1), out=bf(8, 32))),
+        ("groups", lambda: nv.adaln_quantize(bf(9, 64), f32(2, 64), f32(3, 64), 4)),
+        ("shift", lambda: nv.adaln_quantize(bf(8, 64), f32(2, 48), f32(2, 64), 4)),
+        ("shift", lambda: nv.adaln_quantize(bf(8, 64), bf(2, 64), f32(2, 64), 4)),
+        ("dtype", lambda: nv.kv_quantize(f32(2, 8, 128))),
+        ("out scales", lambda: nv.kv_quantize(bf(2, 8, 128), out=(u8(2, 8, 64), u8(2, 8, 9), f32(2)))),
+        ("out head_scales", lambda: nv.kv_quantize(bf(2, 8, 128), out=(u8(2, 8, 64), u8(2, 8, 8), f32(3)))),
+        ("cache codes", lambda: nv.kv_quantize_append(bf(2, 4, 128), (u8(2, 16, 32), u8(2, 16, 8), f32(2)), 0)),
+        ("cache codes", lambda: nv.kv_quantize_append(bf(2, 4, 128), (u8(3, 16, 64), u8(2, 16, 8), f32(2)), 0)),
+        ("outside", lambda: nv.kv_quantize_append(bf(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)), 13)),
+        ("positions", lambda: nv.kv_rope_quantize_append(bf(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)), 0,
+                                                         positions=torch.zeros(4, dtype=torch.int64))),
+        ("out", lambda: nv.kv_dequantize(u8(2, 8, 64), u8(2, 8, 8), f32(2), out=bf(2, 8, 64))),
+        ("v_cache", lambda: nv.kv_attention(bf(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)),
+                                            (u8(2, 16, 64), u8(2, 15, 8), f32(2)))),
+        ("different token counts", lambda: nv.kv_attention(bf(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)),
+                                                           (u8(2, 12, 64), u8(2, 12, 8), f32(2)))),
+        ("kv_tokens", lambda: nv.kv_attention(bf(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)),
+                                              (u8(2, 16, 64), u8(2, 16, 8), f32(2)), kv_tokens=17)),
+        ("q", lambda: nv.kv_attention(f32(2, 4, 128), (u8(2, 16, 64), u8(2, 16, 8), f32(2)),
+                                      (u8(2, 16, 64), u8(2, 16, 8), f32(2)))),
+        ("GPU", lambda: nv.quantize(bf(8, 64))),  # right shapes, but host memory
+        ("GPU", lambda: nv.gemm(q(8, 64), q(4, 64))),
+    ]
+    for what, fn in cases:
+        with pytest.raises(ValueError, match=what):
+            fn()
+

@@ -10,7 +10,10 @@ With the same s_g on both sides, a scale byte or a code may differ from the
 oracle's only where the exact block maximum or element lies within tau of the
 decision boundary between the two values; everything else must be identical,
 and such elements must be rare.  A computed s_g must be the rounding of a
-maximum within tau of the exact one (to one fp32 step)."""
+maximum within tau of the exact one (to one fp32 step), and the codes and scale
+bytes computed with it must be the exact quantization of y under that s_g, with
+the same near-boundary freedom (when s_g equals the oracle's they must equal
+the given-scale call's bytes exactly)."""
 import numpy as np
 import pytest
 import torch
@@ -57,6 +60,9 @@ def _run(x_cpu, shift, scale, rpg, eps, label, check_scale=True):
             am, tm = float(np.abs(y).max()), float(tau.max())
             ulp = float(np.spacing(np.float32(s_o)))
             assert (am - tm) / 2688 - ulp <= float(g) <= (am + tm) / 2688 + ulp, (label, g, s_o, tm)
+            # and the codes / scale bytes of that call are the exact quantization of y under the
+            # kernel's own s_g, up to the same near-boundary freedom
+            check_quant_near_exact(comp[0], comp[1], y, tau, g, label + " (computed s_g)")
         else:
             for u, v in zip(comp[:2], given[:2]):
                 assert torch.equal(u, v)

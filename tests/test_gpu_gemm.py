@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import assert_quant_equal, c_to_f64, check_gemm_bound, dev, log, oracle_input
+from tests.gpu_helpers import assert_quant_equal, c_to_f64, check_gemm_bound, check_gemm_tiles, dev, log, \
+    oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -84,17 +85,7 @@ def test_gemm_config_full_size(cfg):
     wo = oracle.quantize(oracle_input(w))
     assert_quant_equal(aq, ao, "cfg%d A" % cfg)
     assert_quant_equal(wq, wo, "cfg%d W" % cfg)
-    M, N = c.shape
-    rng = np.random.default_rng(cfg)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 6)]))
-    cpu_c = c_to_f64(c)
-    log("config", cfg, "oracle rows", rows.tolist(), "cols", cols.tolist())
-    ref, tot = oracle.gemm_ref(*ao, *wo, rows=rows)
-    w1 = check_gemm_bound(cpu_c[rows], ref, tot, out == torch.bfloat16, "cfg%d rows" % cfg)
-    ref, tot = oracle.gemm_ref(*ao, *wo, cols=cols)
-    w2 = check_gemm_bound(cpu_c[:, cols], ref, tot, out == torch.bfloat16, "cfg%d cols" % cfg)
-    log("config", cfg, "worst err/bound", max(w1, w2))
+    check_gemm_tiles(c_to_f64(c), ao, wo, out == torch.bfloat16, "cfg%d" % cfg, seed=cfg)
     if cfg == 3:  # the fused call equals quantize + gemm bit for bit
         c2 = nv.gemm(nv.quantize(ad), wq, out_dtype=out)
         assert torch.equal(c, c2)
@@ -109,7 +100,7 @@ def test_gemm_deterministic():
 
 def test_gemm_many_tiles_with_ragged_edges():
     """More tiles than workgroups (each walks several tiles), last tile row and
-    column ragged; sampled rows and columns against the oracle."""
+    column ragged; every output tile sampled against the oracle."""
     nv = _nv()
     M, N, K = 16 * 256 + 100, 17 * 256 - 60, 512
     log("gemm many tiles", M, N, K)
@@ -118,12 +109,7 @@ def test_gemm_many_tiles_with_ragged_edges():
     aq, bq = nv.quantize(a.to(dev())), nv.quantize(b.to(dev()))
     c = c_to_f64(nv.gemm(aq, bq, out_dtype=torch.bfloat16))
     ao, bo = oracle.quantize(oracle_input(a)), oracle.quantize(oracle_input(b))
-    rows = np.array([0, 255, 256, 4095, 4096, 4150, M - 1])
-    cols = np.array([0, 3, 255, 256, 4095, 4096, N - 4, N - 1])
-    ref, tot = oracle.gemm_ref(*ao, *bo, rows=rows)
-    check_gemm_bound(c[rows], ref, tot, True, "many tiles rows")
-    ref, tot = oracle.gemm_ref(*ao, *bo, cols=cols)
-    check_gemm_bound(c[:, cols], ref, tot, True, "many tiles cols")
+    check_gemm_tiles(c, ao, bo, True, "many tiles")
 
 
 @pytest.mark.parametrize("K", [48, 512, 1024])
@@ -146,3 +132,29 @@ def test_gemm_every_scale_byte(K):
     c = nv.gemm((t(ac), t(sa), one), (t(bc), t(sb), one), out_dtype=torch.float32)
     ref, tot = oracle.gemm_ref(ac, sa, 1.0, bc, sb, 1.0)
     check_gemm_bound(c_to_f64(c), ref, tot, False, "every scale byte K=%d" % K)
+
+
+def test_fused_act_given_scale_matches_computed():
+    """nvfp4_gemm_fused_act with the activation scale given (NVFP4_SCALE_GIVEN, written
+    beforehand on the stream by nvfp4_global_scale) equals the computed-scale call bit for
+    bit: packed activation, scale and C; and equals quantize + gemm with that scale."""
+    nv = _nv()
+    for cfg, M in ((3, 2048), (2, 1000)):
+        a = workloads.activations(cfg, M=M).to(dev())
+        wq = nv.quantize(workloads.weights(cfg, N=520).to(dev()))
+        c1, q1 = nv.gemm_fused_act(a, wq)
+        sg = nv.global_scale(a)
+        c2, q2 = nv.gemm_fused_act(a, wq, s_g=sg)
+        c3 = nv.gemm(nv.quantize(a, s_g=sg), wq)
+        torch.cuda.synchronize()
+        log("fused_act given scale, cfg", cfg, "M", M)
+        assert q2[2] is sg
+        for u, v in zip(q1, q2):
+            assert torch.equal(u, v)
+        assert torch.equal(c1, c2) and torch.equal(c2, c3)
+        # a different given scale is used as given (saturating codes), not recomputed
+        half = sg * 0.5
+        c4, q4 = nv.gemm_fused_act(a, wq, s_g=half)
+        ref = nv.quantize(a, s_g=half)
+        torch.cuda.synchronize()
+        assert torch.equal(q4[0], ref[0]) and torch.equal(q4[1], ref[1]) and torch.equal(c4, nv.gemm(ref, wq))

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import assert_quant_equal, c_to_f64, check_gemm_bound, dev, log, oracle_input
+from tests.gpu_helpers import assert_quant_equal, c_to_f64, check_gemm_bound, check_gemm_tiles, dev, log, \
+    oracle_input
 
 pytestmark = pytest.mark.gpu
 
@@ -121,7 +122,7 @@ def test_backward_gemms_small(M, N, K):
 def test_backward_gemms_config3_full_size_sampled():
     """The FFN up-projection's dgrad (16384 x 3072, contracting 14336) and wgrad
     (14336 x 3072, contracting 16384) on the fast GEMM path; sampled rows and
-    columns against the oracle."""
+    columns of every output tile against the oracle."""
     nv = _nv()
     a, w, dy = workloads.activations(3), workloads.weights(3), workloads.output_grads(3)
     log("cfg3 backward: dY", tuple(dy.shape))
@@ -133,13 +134,4 @@ def test_backward_gemms_config3_full_size_sampled():
     for c, (ao, bo), lbl in ((dx, (dyo, wto), "dX"),
                              (dw, (oracle.quantize_transposed(oracle_input(dy)),
                                    oracle.quantize_transposed(oracle_input(a))), "dW")):
-        M, N = c.shape
-        rng = np.random.default_rng(M)
-        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 4)]))
-        cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 4)]))
-        cc = c_to_f64(c)
-        log(lbl, "oracle rows", rows.tolist(), "cols", cols.tolist())
-        ref, tot = oracle.gemm_ref(*ao, *bo, rows=rows)
-        check_gemm_bound(cc[rows], ref, tot, True, lbl + " rows")
-        ref, tot = oracle.gemm_ref(*ao, *bo, cols=cols)
-        check_gemm_bound(cc[:, cols], ref, tot, True, lbl + " cols")
+        check_gemm_tiles(c_to_f64(c), ao, bo, True, "cfg3 " + lbl, seed=len(lbl))

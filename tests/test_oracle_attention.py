@@ -105,3 +105,19 @@ def test_attention_output_within_weighted_magnitude():
     out, wabs = oracle.kv_attention(_queries(2, 9, 64, 9, s=4.0), kc, vc, 100, 0.125)
     assert (np.abs(out) <= wabs * (1 + 1e-12)).all()
     assert (wabs <= np.abs(_decode(vc, 100)).max(axis=1, keepdims=True) * (1 + 1e-12)).all()
+
+
+@pytest.mark.parametrize("H,Tq,Tc,T,D", [(2, 5, 80, 70, 32), (1, 3, 300, 257, 128)])
+def test_attention_normaliser_matches_logsumexp(H, Tq, Tc, T, D):
+    """The normaliser sum_j exp(s_j - max s) equals exp(logsumexp(s) - max s) computed by torch
+    (a library routine) from scores formed here out of the decoded rows; it is >= 1."""
+    kc, vc = _caches(H, Tc, D, 3 * Tc + D)
+    q = _queries(H, Tq, D, 7 * H + Tq, s=3.0)
+    scale = 1.0 / np.sqrt(D)
+    _, _, lsum = oracle.kv_attention(q, kc, vc, T, scale, return_norm=True)
+    s = torch.einsum("hqd,htd->hqt", torch.from_numpy(_bf16_vals(q)), torch.from_numpy(_decode(kc, T))) * scale
+    want = torch.exp(torch.logsumexp(s, dim=-1) - s.max(dim=-1).values).numpy()
+    np.testing.assert_allclose(lsum, want, rtol=1e-12)
+    assert (lsum >= 1.0).all()
+    sub, _, lsub = oracle.kv_attention(q, kc, vc, T, scale, q_idx=np.array([2, 0]), return_norm=True)
+    np.testing.assert_array_equal(lsub, lsum[:, [2, 0]])
