@@ -67,6 +67,9 @@ typedef enum {
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
 
+/* Size of the fixed device array that kv_attention_noalloc uses as scratch. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
 #define NVFP4_SCALE_COMPUTE 0 /* compute s_g from the data and write it to *s_g */
 #define NVFP4_SCALE_GIVEN 1   /* use the s_g already stored at *s_g (device) */
 
@@ -299,6 +302,29 @@ nvfp4_status_t kv_attention(const void *q, int64_t heads, int64_t q_tokens, int6
                             const uint8_t *v_codes, const uint8_t *v_scales, const float *v_head_scales,
                             int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, void *out,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_attention for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * without the workspace, the same kernels and results as kv_attention with a
+ * workspace of NVFP4_NOALLOC_SCRATCH_BYTES (32 MiB).  The split-cache partial
+ * results go to a fixed device array of that size inside the library, one per
+ * device, held until the process ends; the call allocates nothing (its first
+ * call on a device looks up that array's address there).  A cache split whose
+ * partial results would exceed the array is not chosen, down to one pass that
+ * needs none, so every size kv_attention accepts runs; shapes outside those
+ * limits give NVFP4_ERR_SHAPE as there.  Nothing in the array needs to start
+ * at zero: every call writes all the partials it reads.  All calls on one
+ * device share the array: calls that overlap in time on one device (different
+ * streams, or several host threads) race and give wrong results; calls on one
+ * stream are ordered and safe.  The stream must belong to a device the
+ * library can run on; NVFP4_ERR_LAUNCH if the array cannot be found there.
+ */
+nvfp4_status_t kv_attention_noalloc(const void *q, int64_t heads, int64_t q_tokens, int64_t head_dim,
+                                    const uint8_t *k_codes, const uint8_t *k_scales, const float *k_head_scales,
+                                    const uint8_t *v_codes, const uint8_t *v_scales, const float *v_head_scales,
+                                    int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, void *out,
+                                    void *stream);
 
 /*
  * Workspace bytes at which kv_attention takes its preferred cache split for

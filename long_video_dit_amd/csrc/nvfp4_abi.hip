@@ -297,4 +297,17 @@ nvfp4_status_t kv_attention(const void* q, int64_t heads, int64_t q_tokens, int6
                                              ws, (hipStream_t)stream));
 }
 
+nvfp4_status_t kv_attention_noalloc(const void* q, int64_t heads, int64_t q_tokens, int64_t head_dim,
+                                    const uint8_t* k_codes, const uint8_t* k_scales, const float* k_head_scales,
+                                    const uint8_t* v_codes, const uint8_t* v_scales, const float* v_head_scales,
+                                    int64_t cache_tokens, int64_t kv_tokens, float softmax_scale, void* out,
+                                    void* stream) {
+  nvfp4_status_t st = check_attention(q, heads, q_tokens, head_dim, k_codes, k_scales, k_head_scales, v_codes,
+                                      v_scales, v_head_scales, cache_tokens, kv_tokens, softmax_scale, out);
+  if (st != NVFP4_OK) return st;
+  return from_hip(nvfp4::launch_kv_attention_noalloc(q, k_codes, k_scales, k_head_scales, v_codes, v_scales,
+                                                     v_head_scales, heads, q_tokens, cache_tokens, kv_tokens,
+                                                     softmax_scale, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

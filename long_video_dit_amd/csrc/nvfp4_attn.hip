@@ -45,8 +45,19 @@
 //      c ^ (8 (token % 4) + 2 ((token / 4) % 4)).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "../../include/nvfp4.h"
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
+
+// Scratch of kv_attention_noalloc, for callers that cannot allocate: the
+// split-cache partial results (fp32 O, m, l per range and query) live in this
+// fixed array instead of a caller workspace.  Each device the library runs on
+// holds its own copy until the process ends.  Host code never passes this name
+// to a kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
 
 namespace nvfp4 {
 
@@ -429,6 +440,59 @@ hipError_t launch_kv_attention(const void* q, const uint8_t* k_codes, const uint
   return launch_kernel(attn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        (const float*)part_o, (const float2*)part_ml, v_hs, sp.splits, (int)heads, (int)q_tokens,
                        (__bf16*)out);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up with that device current on the
+// first call for it.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_kv_attention_noalloc(const void* q, const uint8_t* k_codes, const uint8_t* k_scales,
+                                       const float* k_hs, const uint8_t* v_codes, const uint8_t* v_scales,
+                                       const float* v_hs, int64_t heads, int64_t q_tokens, int64_t cache_tokens,
+                                       int64_t kv_tokens, float scale, void* out, hipStream_t stream) {
+  if (q_tokens == 0) return hipSuccess;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(stream, &ws);
+  if (e != hipSuccess) return e;
+  // The same kernels as kv_attention with a workspace of the scratch's size:
+  // no split whose partial results would not fit is chosen, so every size
+  // kv_attention accepts runs (one pass needs no scratch at all).
+  return launch_kv_attention(q, k_codes, k_scales, k_hs, v_codes, v_scales, v_hs, heads, q_tokens, cache_tokens,
+                             kv_tokens, scale, out, ws, (int64_t)NVFP4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // namespace nvfp4

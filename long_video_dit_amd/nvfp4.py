@@ -41,8 +41,12 @@ SIGNATURES = {
     "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kv_attention": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                           ctypes.c_size_t, _P]),
+    "kv_attention_noalloc": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P,
+                                  _P]),
     "kv_attention_workspace_size": (_I, [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
 }
+# NVFP4_NOALLOC_SCRATCH_BYTES: the fixed scratch array of kv_attention_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -450,3 +454,18 @@ def kv_attention(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None, work
           scale, _ptr(o), _ptr(workspace) if workspace.numel() else None, workspace.numel(), _stream(dev))
     return o
 
+
+def kv_attention_noalloc(q, k_cache, v_cache, kv_tokens=None, scale=None, out=None):
+    """kv_attention for callers that cannot allocate: the library's fixed device scratch
+    (NOALLOC_SCRATCH_BYTES) holds the split-cache partials; the result equals kv_attention with
+    a workspace of that size.  Pass `out` to allocate nothing here either.  Calls that overlap
+    in time on one device race (they share the scratch)."""
+    ops = _Operands()
+    H, Tq, D, T, kv_tokens, scale = _attention_args(ops, q, k_cache, v_cache, kv_tokens, scale, out)
+    dev = ops.device()
+    o = torch.empty_like(q) if out is None else out
+    kc, ks, kh = k_cache
+    vc, vs, vh = v_cache
+    _call("kv_attention_noalloc", _ptr(q), H, Tq, D, _ptr(kc), _ptr(ks), _ptr(kh), _ptr(vc), _ptr(vs), _ptr(vh), T,
+          kv_tokens, scale, _ptr(o), _stream(dev))
+    return o

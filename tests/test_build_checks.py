@@ -116,6 +116,12 @@ def test_validation_errors_launch_nothing():
     assert kva(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, odd, None) == nv.ERR_ALIGN
     assert lib.kv_attention(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, odd, 64,
                             None) == nv.ERR_ALIGN  # workspace
+    kn = lib.kv_attention_noalloc  # the no-allocation variant validates the same way, before any lookup
+    assert kn(buf, 2, 8, 64, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_SHAPE
+    assert kn(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 33, 0.1, buf, None) == nv.ERR_SHAPE
+    assert kn(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, float("inf"), buf, None) == nv.ERR_SHAPE
+    assert kn(buf, 2, 8, 128, buf, buf, buf, None, buf, buf, 32, 32, 0.1, buf, None) == nv.ERR_NULL
+    assert kn(buf, 2, 8, 128, buf, buf, buf, buf, buf, buf, 32, 32, 0.1, odd, None) == nv.ERR_ALIGN
     n = ctypes.c_size_t(7)
     assert lib.kv_attention_workspace_size(2, 8, 64, 32, ctypes.byref(n)) == nv.ERR_SHAPE
     assert lib.kv_attention_workspace_size(2, 8, 128, 0, ctypes.byref(n)) == nv.ERR_SHAPE
@@ -254,3 +260,8 @@ def test_binding_rejects_mismatched_operands():
         with pytest.raises(ValueError, match=what):
             fn()
 
+
+def test_noalloc_scratch_size_matches_header():
+    from long_video_dit_amd import nvfp4 as nv
+    m = re.search(r"#define NVFP4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == nv.NOALLOC_SCRATCH_BYTES
