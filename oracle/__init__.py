@@ -13,6 +13,9 @@ linears and an NVFP4 KV cache but fix no numeric detail.
 
 Arrays are numpy: float32 arrays are fp32 tensors, uint16 arrays are bf16
 bit patterns.  Every function pinned by the tests in ``tests/test_oracle_*``.
+FourOverSix block scaling (``four_over_six=True``) is a reading of a name the
+pages give without a definition (d9249.github.io review): its rule is pinned
+by exact brute force of that rule, not by the pages.
 """
 import ctypes
 import os
@@ -61,6 +64,10 @@ def _load():
         "orc_amax": (c_i, [c_p, c_i, c_i64, c_p]),
         "orc_quantize_with_scale": (c_i, [c_p, c_i, c_i64, c_i64, c_f, c_p, c_p]),
         "orc_quantize": (c_i, [c_p, c_i, c_i64, c_i64, c_p, c_p, c_p]),
+        "orc_block_scale4": (c_i, [c_d, c_f]),
+        "orc_quantize_4o6_with_scale": (c_i, [c_p, c_i, c_i64, c_i64, c_f, c_p, c_p]),
+        "orc_quantize_4o6": (c_i, [c_p, c_i, c_i64, c_i64, c_p, c_p, c_p]),
+        "orc_kv_quantize_4o6": (c_i, [c_p, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
         "orc_dequantize": (c_i, [c_p, c_p, c_f, c_i64, c_i64, c_p, c_i]),
         "orc_gemm_ref": (c_i, [c_p, c_p, c_f, c_p, c_p, c_f, c_i64, c_i64, c_i64,
                                c_p, c_i64, c_p, c_i64, c_p, c_p]),
@@ -145,8 +152,18 @@ def amax(x):
     return np.float32(out.value)
 
 
-def quantize(x, s_g=None):
-    """x [rows, k] -> (codes uint8 [rows, k/2], scales uint8 [rows, k/16], s_g float32)."""
+def block_scale4(amax_b, s_g):
+    """E4M3 byte of RNE_SAT(amax_b / (4 s_g)), the second FourOverSix candidate."""
+    return _load().orc_block_scale4(float(amax_b), float(np.float32(s_g)))
+
+
+def quantize(x, s_g=None, four_over_six=False):
+    """x [rows, k] -> (codes uint8 [rows, k/2], scales uint8 [rows, k/16], s_g float32).
+
+    four_over_six: FourOverSix block scaling (a reading: the pages name the backend,
+    d9249.github.io review, but do not define it): per block the scale mapping the block
+    maximum to 6 or the one mapping it to 4, whichever dequantizes with the smaller exact sum
+    of squared errors (ties: 6); s_g as usual."""
     x = np.ascontiguousarray(x)
     if x.ndim != 2:
         raise OracleError("quantize expects a 2-D array")
@@ -154,12 +171,13 @@ def quantize(x, s_g=None):
     codes = np.zeros((rows, k // 2), np.uint8)
     scales = np.zeros((rows, k // 16), np.uint8)
     lib = _load()
+    full, given = ((lib.orc_quantize_4o6, lib.orc_quantize_4o6_with_scale) if four_over_six else
+                   (lib.orc_quantize, lib.orc_quantize_with_scale))
     if s_g is None:
         sg = ctypes.c_float(0.0)
-        _check(lib.orc_quantize(_ptr(x), _dtype_of(x), rows, k, _ptr(codes), _ptr(scales), ctypes.byref(sg)))
+        _check(full(_ptr(x), _dtype_of(x), rows, k, _ptr(codes), _ptr(scales), ctypes.byref(sg)))
         return codes, scales, np.float32(sg.value)
-    _check(lib.orc_quantize_with_scale(_ptr(x), _dtype_of(x), rows, k, float(np.float32(s_g)),
-                                       _ptr(codes), _ptr(scales)))
+    _check(given(_ptr(x), _dtype_of(x), rows, k, float(np.float32(s_g)), _ptr(codes), _ptr(scales)))
     return codes, scales, np.float32(s_g)
 
 
@@ -252,8 +270,9 @@ def gemm_ref(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, rows=None, cols=N
     return ref, tot
 
 
-def kv_quantize(kv):
-    """kv bf16 bits uint16 [H, T, D] -> (codes [H,T,D/2], scales [H,T,D/16], head_scales [H])."""
+def kv_quantize(kv, four_over_six=False):
+    """kv bf16 bits uint16 [H, T, D] -> (codes [H,T,D/2], scales [H,T,D/16], head_scales [H]);
+    four_over_six as in quantize (per-head scales as usual)."""
     kv = np.ascontiguousarray(kv)
     if kv.dtype != np.uint16 or kv.ndim != 3:
         raise OracleError("kv_quantize expects uint16 bf16 bits [H, T, D]")
@@ -261,7 +280,8 @@ def kv_quantize(kv):
     codes = np.zeros((H, T, D // 2), np.uint8)
     scales = np.zeros((H, T, D // 16), np.uint8)
     hs = np.zeros(H, np.float32)
-    _check(_load().orc_kv_quantize(_ptr(kv), H, T, D, _ptr(codes), _ptr(scales), _ptr(hs)))
+    fn = _load().orc_kv_quantize_4o6 if four_over_six else _load().orc_kv_quantize
+    _check(fn(_ptr(kv), H, T, D, _ptr(codes), _ptr(scales), _ptr(hs)))
     return codes, scales, hs
 
 

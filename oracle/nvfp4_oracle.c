@@ -32,6 +32,7 @@
  * input or a bad shape.  Arrays are host memory, row-major, reduction axis
  * contiguous.  OpenMP runs over rows.
  */
+#include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 #include <stdint.h>
@@ -123,9 +124,9 @@ float orc_global_scale_f64(double amax) {
  * midpoint(b-1, b) * 6 * s_g, exact in fp64 (<= 5 + 2 + 24 significant
  * bits).  At a midpoint the even byte wins; anything above the last
  * midpoint (432) saturates to 0x7E = 448; a zero s_g or zero block gives 0. */
-int orc_block_scale(double amax_b, float s_g) {
+static int block_scale_div(double amax_b, float s_g, double div) {
   if (s_g == 0.0f || amax_b == 0.0) return 0;
-  double den = 6.0 * (double)s_g;
+  double den = div * (double)s_g;
   int best = 0;
   for (int b = 1; b < 127; b++) {
     double mid = 0.5 * (orc_e4m3_value(b - 1) + orc_e4m3_value(b)) * den;
@@ -133,6 +134,13 @@ int orc_block_scale(double amax_b, float s_g) {
   }
   return best;
 }
+
+int orc_block_scale(double amax_b, float s_g) { return block_scale_div(amax_b, s_g, 6.0); }
+
+/* The same rounding of amax_b / (4 s_g): the scale that maps the block maximum
+ * to 4 instead of 6 (the second candidate of FourOverSix below); mid * 4 * s_g
+ * is exact in fp64 as well. */
+int orc_block_scale4(double amax_b, float s_g) { return block_scale_div(amax_b, s_g, 4.0); }
 
 /* Element code: sign(x) | RNE_SAT_E2M1(|x| / S) with S = val(s_b) * s_g
  * (exact in fp64).  |x| is compared with midpoint(i-1, i) * S, exact in
@@ -230,6 +238,115 @@ int orc_quantize(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *cod
   }
   *s_g = orc_global_scale_f64(m);
   return orc_quantize_with_scale(x, dtype, rows, k, *s_g, codes, scales);
+}
+
+/* ---- FourOverSix block scaling ---------------------------------------- */
+
+/* The pages name a FourOverSix backend (a `fouroversix` directory) and an
+ * NVFP4 checkpoint `model_4o6.pt` (d9249.github.io review, sections on the
+ * evidence and on the practical reading) but do not define it.  Reading used
+ * here (not fixed by the pages): s_g is the usual per-tensor scale; for each
+ * 16-element block two candidate scale bytes are formed, s6 = RNE_SAT(amax_b /
+ * (6 s_g)) (the standard one) and s4 = RNE_SAT(amax_b / (4 s_g)), the block is
+ * encoded under each with the usual E2M1 rounding, and the candidate whose
+ * dequantized block val(q) val(s) s_g has the smaller sum of squared errors
+ * against the input is kept; equal errors keep s6.  The stored format is plain
+ * NVFP4, so dequantization and the GEMM are unchanged. */
+
+/* Exponent of the lowest and of the highest set bit of a finite nonzero double. */
+static int low_bit_exp(double v) {
+  int e;
+  double m = frexp(fabs(v), &e); /* |v| = m 2^e, m in [0.5, 1) */
+  uint64_t u = (uint64_t)ldexp(m, 53);
+  return e - 53 + __builtin_ctzll(u);
+}
+
+static int high_bit_exp(double v) {
+  int e;
+  frexp(fabs(v), &e);
+  return e - 1;
+}
+
+/* Sign of sum_i (x_i - a_i)^2 - sum_i (x_i - b_i)^2, exactly, for exact double
+ * values.  Elements with a_i == b_i contribute nothing; for the others every
+ * nonzero value is an integer multiple of 2^lo (lo the lowest set bit among
+ * them), and (x - a)^2 - (x - b)^2 = (b - a)(2x - a - b) is summed in 128-bit
+ * integers.  Returns -2 if the values span more than 56 bits (then the sum
+ * could overflow; it cannot happen for the values of one block). */
+static int cmp_sq_err(const double *x, const double *a, const double *b, int n) {
+  int lo = INT_MAX, hi = INT_MIN;
+  for (int i = 0; i < n; i++) {
+    if (a[i] == b[i]) continue;
+    const double v[3] = {x[i], a[i], b[i]};
+    for (int j = 0; j < 3; j++)
+      if (v[j] != 0.0) {
+        if (low_bit_exp(v[j]) < lo) lo = low_bit_exp(v[j]);
+        if (high_bit_exp(v[j]) > hi) hi = high_bit_exp(v[j]);
+      }
+  }
+  if (lo == INT_MAX) return 0;
+  if (hi - lo > 56) return -2;
+  __int128 d = 0;
+  for (int i = 0; i < n; i++) {
+    if (a[i] == b[i]) continue;
+    const __int128 X = (__int128)(int64_t)ldexp(x[i], -lo), A = (__int128)(int64_t)ldexp(a[i], -lo),
+                   B = (__int128)(int64_t)ldexp(b[i], -lo);
+    d += (B - A) * (2 * X - A - B);
+  }
+  return d > 0 ? 1 : (d < 0 ? -1 : 0);
+}
+
+/* FourOverSix quantization of rows x k elements with a given s_g. */
+int orc_quantize_4o6_with_scale(const void *x, int dtype, int64_t rows, int64_t k, float s_g,
+                                uint8_t *codes, uint8_t *scales) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t blk = 0; blk < k / 16; blk++) {
+      double v[16], y6[16], y4[16];
+      int c6[16], c4[16];
+      double amax_b = 0.0;
+      for (int i = 0; i < 16; i++) {
+        v[i] = load_elem(x, dtype, r * k + blk * 16 + i);
+        if (!isfinite(v[i])) bad = 1;
+        if (fabs(v[i]) > amax_b) amax_b = fabs(v[i]);
+      }
+      const int s6 = orc_block_scale(amax_b, s_g), s4 = orc_block_scale4(amax_b, s_g);
+      const double S6 = orc_e4m3_value(s6) * (double)s_g, S4 = orc_e4m3_value(s4) * (double)s_g; /* exact */
+      for (int i = 0; i < 16; i++) {
+        c6[i] = orc_e2m1_code(v[i], S6);
+        c4[i] = orc_e2m1_code(v[i], S4);
+        y6[i] = orc_e2m1_value(c6[i]) * S6; /* exact: <= 2 + 4 + 24 significant bits */
+        y4[i] = orc_e2m1_value(c4[i]) * S4;
+      }
+      int use4 = 0;
+      if (s4 != s6) {
+        const int c = cmp_sq_err(v, y4, y6, 16); /* sign of E(s4) - E(s6) */
+        if (c == -2) bad = 2;
+        use4 = (c == -1);
+      }
+      const int *cc = use4 ? c4 : c6;
+      scales[r * (k / 16) + blk] = (uint8_t)(use4 ? s4 : s6);
+      for (int i = 0; i < 16; i += 2)
+        codes[r * (k / 2) + blk * 8 + i / 2] = (uint8_t)(cc[i] | (cc[i + 1] << 4));
+    }
+  }
+  return bad == 1 ? ORC_ERR_NONFINITE : (bad ? ORC_ERR_SHAPE : ORC_OK);
+}
+
+/* FourOverSix with the per-tensor scale computed as usual (amax / 2688). */
+int orc_quantize_4o6(const void *x, int dtype, int64_t rows, int64_t k, uint8_t *codes, uint8_t *scales,
+                     float *s_g) {
+  if (rows < 0 || k <= 0 || k % 16 != 0) return ORC_ERR_SHAPE;
+  double m = 0.0;
+  for (int64_t i = 0; i < rows * k; i++) {
+    double v = load_elem(x, dtype, i);
+    if (!isfinite(v)) return ORC_ERR_NONFINITE;
+    if (fabs(v) > m) m = fabs(v);
+  }
+  *s_g = orc_global_scale_f64(m);
+  return orc_quantize_4o6_with_scale(x, dtype, rows, k, *s_g, codes, scales);
 }
 
 /* adaLN of layer-normalized rows (the pages list a unified RoPE + adaLN kernel
@@ -356,6 +473,24 @@ int orc_kv_quantize(const uint16_t *kv, int64_t heads, int64_t tokens, int64_t h
     st = orc_quantize_with_scale(xh, ORC_BF16, tokens, head_dim, head_scales[h],
                                  codes + h * tokens * (head_dim / 2),
                                  scales + h * tokens * (head_dim / 16));
+    if (st) return st;
+  }
+  return ORC_OK;
+}
+
+/* The same per-head scales with FourOverSix block scaling (see above). */
+int orc_kv_quantize_4o6(const uint16_t *kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                        uint8_t *codes, uint8_t *scales, float *head_scales) {
+  if (heads <= 0 || tokens < 0 || head_dim <= 0 || head_dim % 16 != 0) return ORC_ERR_SHAPE;
+  for (int64_t h = 0; h < heads; h++) {
+    const uint16_t *xh = kv + h * tokens * head_dim;
+    float amax;
+    int st = orc_amax(xh, ORC_BF16, tokens * head_dim, &amax);
+    if (st) return st;
+    head_scales[h] = orc_global_scale(amax);
+    st = orc_quantize_4o6_with_scale(xh, ORC_BF16, tokens, head_dim, head_scales[h],
+                                     codes + h * tokens * (head_dim / 2),
+                                     scales + h * tokens * (head_dim / 16));
     if (st) return st;
   }
   return ORC_OK;

@@ -162,3 +162,30 @@ def dequant_bf16_bits(code, sb, s_g):
     """bf16 bits of RN(val(code) val(sb) s_g); the code's sign bit is kept for zeros."""
     v = abs(dequant_exact(code, sb, s_g))
     return round_bf16_bits(v) | (0x8000 if int(code) & 8 else 0)
+
+
+def block_scale4(amax_b, s_g):
+    """E4M3 byte nearest to amax_b / (4 s_g), ties to the even byte (the FourOverSix candidate
+    that maps the block maximum to 4)."""
+    if s_g == 0 or amax_b == 0:
+        return 0
+    return nearest_even(E4M3_VALUES, F(float(amax_b)) / (4 * F(float(s_g))))
+
+
+def sq_err(blk, codes, sb, s_g):
+    """Exact sum of squared differences between a block and its dequantized codes."""
+    return sum((F(float(v)) - dequant_exact(c, sb, s_g)) ** 2 for v, c in zip(blk, codes))
+
+
+def four_over_six_block(blk, s_g):
+    """FourOverSix reading for one 16-value block under s_g: encode with the scale for 6 and
+    with the scale for 4, keep the one with the smaller exact squared error (ties: 6).
+    Returns (nibbles, scale byte, err6, err4)."""
+    amax_b = max(abs(v) for v in blk)
+    out = []
+    for sb in (block_scale(amax_b, s_g), block_scale4(amax_b, s_g)):
+        S = E4M3_VALUES[sb] * F(float(s_g))
+        codes = [e2m1_code(v, S) for v in blk]
+        out.append((codes, sb, sq_err(blk, codes, sb, s_g)))
+    (c6, s6, e6), (c4, s4, e4) = out
+    return (c4, s4, e6, e4) if e4 < e6 else (c6, s6, e6, e4)
