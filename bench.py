@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true", help="skip the quantize / KV-cache bandwidth lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--oracle-sample-rows", type=int, default=0,
+                   help=argparse.SUPPRESS)  # internal: time the oracle sample in this process (no GPU) and exit
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the step: time every workload (quantize, GEMM, KV cache) and the oracle "
                         "on a bounded sample of each, one JSON line")
@@ -74,6 +76,22 @@ def parse():
 
 def events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+FLUSH_BYTES = 1 << 30  # written between cold calls: four times the 256 MB Infinity Cache (MALL)
+
+
+def time_cold(torch, fn, flush, steps):
+    """Average ms of fn() with the caches cold: before each call a 1 GiB buffer is
+    written (evicting L2 and MALL), outside the HIP-event window of the call."""
+    pairs = [events(torch, 2) for _ in range(steps)]
+    for s, e in pairs:
+        flush.fill_(1.0)
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in pairs) / steps
 
 
 def time_calls(torch, fn, steps, warmup):
@@ -109,6 +127,13 @@ def gemm_traffic(root):
 
 def main():
     args = parse()
+    if args.oracle_sample_rows:
+        root = os.path.dirname(os.path.abspath(__file__))
+        sys.path.insert(0, root)
+        import workloads
+        dt, threads = oracle_sample(workloads, args.oracle_sample_rows)
+        print(json.dumps({"seconds": dt, "threads": threads}), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the NVFP4 hot path runs on a single MI355X here; "
               "--gpus %d is not supported (multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
@@ -196,7 +221,22 @@ def main():
                                                                              achieved))
 
     if not args.no_secondary:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        cold_ms = time_cold(torch, step, flush, args.steps)
+        quant = lambda: nvfp4.quantize(a, out=aq[:2], s_g_out=aq[2])
+        cold_q = time_cold(torch, quant, flush, 10)
+        warm_q = time_calls(torch, quant, 10, 2)
+        del flush
         out["secondary"] = secondary(torch, nvfp4, workloads, dev, a, aq)
+        qb = M * K * (B_AMAX + B_ENCODE)
+        out["secondary"]["cold"] = {
+            "note": "a 1 GiB buffer written before every call, outside the event window (the MALL is 256 MB)",
+            "step_ffn_up": {"ms": round(cold_ms, 4), "TFLOP/s": round(flop / (cold_ms * 1e-3) / 1e12, 1),
+                            "warm_ms": round(ms_per_step, 4)},
+            "quantize_ffn_up_act": {"shape": [M, K], "ms": round(cold_q, 4),
+                                    "GB/s": round(qb / (cold_q * 1e-3) / 1e9, 1), "warm_ms": round(warm_q, 4),
+                                    "warm_GB/s": round(qb / (warm_q * 1e-3) / 1e9, 1)},
+            **out["secondary"].pop("_cold")}
     if args.copy_calibration:
         x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
@@ -222,11 +262,21 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     q4 = (torch.empty(M4, K4 // 2, dtype=torch.uint8, device=dev),
           torch.empty(M4, K4 // 16, dtype=torch.uint8, device=dev),
           torch.empty(1, dtype=torch.float32, device=dev))
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cold = {}
+    ms_c = time_cold(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2]), flush, 10)
     ms = time_calls(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2]), 10, 2)
     n = a4.numel()
+    cold["quantize_ffn_down_act"] = {"shape": [M4, K4], "ms": round(ms_c, 4),
+                                     "GB/s": round(n * (B_AMAX + B_ENCODE) / (ms_c * 1e-3) / 1e9, 1)}
     res["quantize_ffn_down_act"] = {"shape": [M4, K4], "ms": round(ms, 4),
                                     "GB/s": round(n * (B_AMAX + B_ENCODE) / (ms * 1e-3) / 1e9, 1),
                                     "bytes_per_elem": B_AMAX + B_ENCODE}
+    # the same with FourOverSix block scaling (two candidate scales per block)
+    ms = time_calls(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2], four_over_six=True), 10, 2)
+    res["quantize_ffn_down_act_four_over_six"] = {"shape": [M4, K4], "ms": round(ms, 4),
+                                                  "GB/s": round(n * (B_AMAX + B_ENCODE) / (ms * 1e-3) / 1e9, 1),
+                                                  "bytes_per_elem": B_AMAX + B_ENCODE}
     del a4, q4
     # NVFP4 KV cache: K and V bf16 [24, 65536, 128], quantize + dequantize
     k, v = workloads.kv_cache()
@@ -242,10 +292,20 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
         nvfp4.kv_dequantize(*qv, out=ov)
 
     ms = time_calls(torch, rt, 10, 2)
+    ms_c = time_cold(torch, rt, flush, 10)
     n = 2 * k.numel()
     res["kv_cache_roundtrip"] = {"shape": [H, T, D], "tensors": 2, "ms": round(ms, 4),
                                  "GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (ms * 1e-3) / 1e9, 1),
                                  "bytes": n * (B_AMAX + B_ENCODE + B_DEQUANT)}
+    cold["kv_cache_roundtrip"] = {"ms": round(ms_c, 4),
+                                  "GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (ms_c * 1e-3) / 1e9, 1)}
+    ms_qc = time_cold(torch, lambda: nvfp4.kv_quantize(k, out=qk), flush, 10)
+    ms_dc = time_cold(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), flush, 10)
+    cold["kv_quantize"] = {"ms": round(ms_qc, 4),
+                           "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_qc * 1e-3) / 1e9, 1)}
+    cold["kv_dequantize"] = {"ms": round(ms_dc, 4), "GB/s": round(k.numel() * B_DEQUANT / (ms_dc * 1e-3) / 1e9, 1)}
+    del flush
+    res["_cold"] = cold
     # attention of 4,096 new queries per head over the whole packed cache (K and V quantized above)
     Tq = 4096
     qa = workloads.attention_queries(H, Tq, D).to(dev)
@@ -269,7 +329,10 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     del qa, oa, wsa, kn
     ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
+    ms_q46 = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk, four_over_six=True), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}
+    res["kv_quantize_four_over_six"] = {
+        "ms": round(ms_q46, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q46 * 1e-3) / 1e9, 1)}
     res["kv_dequantize"] = {"ms": round(ms_d, 4), "GB/s": round(k.numel() * B_DEQUANT / (ms_d * 1e-3) / 1e9, 1)}
     # backward of the FFN up-projection: dY [16384, 14336] quantized along its rows (the wgrad
     # operand), dX = dY W (contracting 14336) and dW = dY^T A (contracting 16384)
@@ -500,11 +563,23 @@ def settle(torch, fn, seconds=SETTLE_S):
         torch.cuda.synchronize()
 
 
-def cpu_baseline(workloads, M, N, K, rows=8192):
+def cpu_model():
+    """The host CPU's model string (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_sample(workloads, rows):
     """The CPU oracle (test infrastructure) on a bounded sample of the step:
-    quantize `rows` activation rows with the tensor's s_g and compute their
-    reference GEMM rows against all N weight rows (weights quantized once,
-    not timed), as TFLOP/s of the same 2 M N K metric."""
+    the amax of the whole activation, quantization of its first `rows` rows
+    with that scale, and their fp64 reference GEMM rows against all weight
+    rows (weights quantized once, not timed).  Returns (seconds, threads)."""
     import numpy as np
     import oracle
 
@@ -515,11 +590,31 @@ def cpu_baseline(workloads, M, N, K, rows=8192):
     g = oracle.global_scale(oracle.amax(a))
     ac, as_, _ = oracle.quantize(np.ascontiguousarray(a[:rows]), s_g=g)
     oracle.gemm_ref(ac, as_, g, wc, ws, wg)
-    dt = time.perf_counter() - t0
-    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "amax of the full A [%d, %d], quantize of its first %d rows, fp64 reference GEMM of those "
-                      "rows against all %d weight rows (K = %d)" % (M, K, rows, N, K)}
+    return time.perf_counter() - t0, oracle.num_threads()
+
+
+def cpu_baseline(workloads, M, N, K, rows=8192, rows_1t=128):
+    """The oracle on the host's cores (all threads, `rows` rows) and on one thread
+    (a child process with OMP_NUM_THREADS=1, `rows_1t` rows), each as TFLOP/s of
+    the same 2 M N K metric scaled by the rows it computed."""
+    import subprocess
+
+    dt, threads = oracle_sample(workloads, rows)
+    sample = ("amax of the full A [%d, %d], quantize of its first %%d rows, fp64 reference GEMM of those rows "
+              "against all %d weight rows (K = %d)" % (M, K, N, K))
+    out = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 2), "sample": sample % rows, "cpu_model": cpu_model(),
+           "host_cpus": os.cpu_count()}
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-sample-rows", str(rows_1t)],
+                       env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode == 0:
+        d = json.loads(r.stdout.strip().splitlines()[-1])
+        out["single_thread"] = {"value": round(2.0 * rows_1t * N * K / d["seconds"] / 1e12, 6), "cores": d["threads"],
+                                "seconds": round(d["seconds"], 2), "sample": sample % rows_1t}
+    else:
+        log("single-thread oracle run failed:", r.stderr[-500:])
+    return out
 
 
 if __name__ == "__main__":

@@ -72,6 +72,19 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
 
 #define NVFP4_SCALE_COMPUTE 0 /* compute s_g from the data and write it to *s_g */
 #define NVFP4_SCALE_GIVEN 1   /* use the s_g already stored at *s_g (device) */
+/*
+ * FourOverSix block scaling, OR-ed into the flags of the calls that list it.
+ * The pages name a FourOverSix backend (a `fouroversix` directory) and an NVFP4
+ * checkpoint `model_4o6.pt` (d9249.github.io review, sections on the evidence
+ * and on the practical reading) without defining it; the rule here is a
+ * reading: s_g as usual; per 16-element block the scale byte is either the
+ * usual s6 = RNE_SAT(amax_b / (6 s_g)) or s4 = RNE_SAT(amax_b / (4 s_g)),
+ * whichever gives the dequantized block val(q) val(s) s_g the smaller exact
+ * sum of squared errors against the input (equal errors: s6), with the codes
+ * rounded as usual under the kept scale.  The output is ordinary NVFP4:
+ * dequantize, GEMM and attention read it unchanged.
+ */
+#define NVFP4_FOUR_OVER_SIX 2
 
 /* Version of this ABI (NVFP4_ABI_VERSION). */
 int nvfp4_abi_version(void);
@@ -100,6 +113,8 @@ nvfp4_status_t nvfp4_global_scale(const void *x, nvfp4_dtype_t dtype, int64_t ro
  * Quantize x [rows][k] (dtype F32 or BF16, row-major) to NVFP4.
  *   codes   [rows][k/2]  u8 out      scales [rows][k/16] u8 out
  *   s_g     [1] fp32: out with NVFP4_SCALE_COMPUTE, in with NVFP4_SCALE_GIVEN
+ *   flags   NVFP4_SCALE_COMPUTE or NVFP4_SCALE_GIVEN, optionally
+ *           | NVFP4_FOUR_OVER_SIX
  * Per the arXiv abstract (W4A4 NVFP4 inference: weights and activations
  * quantized).  rows == 0 is allowed (COMPUTE then writes s_g = 0).  With
  * COMPUTE the call runs three kernels (amax partials, s_g finalize, encode);
@@ -116,6 +131,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  *   s_g      [1] fp32: out with NVFP4_SCALE_COMPUTE (the same value as for x
  *            itself: the amax does not depend on the layout), in with
  *            NVFP4_SCALE_GIVEN
+ *   flags    as for nvfp4_quantize (NVFP4_FOUR_OVER_SIX allowed)
  * Bit-identical to nvfp4_quantize of a transposed copy of x, without
  * writing that copy.  These are the operands of the backward GEMMs of a
  * linear Y = X W^T in nn.Linear layout (nvfp4_gemm contracts over the
@@ -153,7 +169,8 @@ nvfp4_status_t nvfp4_quantize_transposed(const void *x, nvfp4_dtype_t dtype, int
  * optimizations; this is its adaLN half, fused with the activation
  * quantization that follows it (the modulated activation never goes to HBM).
  * Two passes over x (amax, then encode), the amax partials kept in the codes
- * buffer.  Requires k % 16 == 0, 16 <= k <= 4096, rows < 2^33, rows_per_group >= 1,
+ * buffer.  flags: NVFP4_SCALE_COMPUTE or NVFP4_SCALE_GIVEN only (no
+ * FourOverSix here).  Requires k % 16 == 0, 16 <= k <= 4096, rows < 2^33, rows_per_group >= 1,
  * 0 <= eps finite; shift and scale 16-byte aligned.  rows == 0 is allowed
  * (COMPUTE then writes s_g = 0).
  */
@@ -194,7 +211,8 @@ nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
  *   flags NVFP4_SCALE_GIVEN:   a_sg [1] is an input, e.g. written earlier on the
  *         stream by nvfp4_global_scale (the scale never leaves the device);
  *   a_codes [M][K/2], a_scales [M][K/16]: the packed activation, outputs,
- *         bit-identical to nvfp4_quantize with the same flags and a_sg.
+ *         bit-identical to nvfp4_quantize with the same flags and a_sg;
+ *   flags may add NVFP4_FOUR_OVER_SIX (the activation's block scaling).
  * The packed activation is required, not optional: the GEMM reads it back (from
  * L2 / MALL) and the library allocates nothing, so the caller owns that memory.
  * One call enqueues, on `stream`, amax and finalize kernels (COMPUTE only), the
@@ -218,6 +236,16 @@ nvfp4_status_t nvfp4_gemm_fused_act(const void *a, nvfp4_dtype_t a_dtype, int64_
  */
 nvfp4_status_t kv_quantize(const void *kv, int64_t heads, int64_t tokens, int64_t head_dim,
                            uint8_t *codes, uint8_t *scales, float *head_scales, void *stream);
+
+/*
+ * kv_quantize with FourOverSix block scaling (NVFP4_FOUR_OVER_SIX): the same
+ * per-head scales, and per block the better of the two candidate scale bytes.
+ * Same arguments and rules as kv_quantize.  The pages pair the FourOverSix
+ * backend with the NVFP4 inference path (d9249.github.io review); its use on
+ * the KV cache is this library's reading.
+ */
+nvfp4_status_t kv_quantize_four_over_six(const void *kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                                         uint8_t *codes, uint8_t *scales, float *head_scales, void *stream);
 
 /*
  * Append to an NVFP4 KV cache in place: kv_new [heads][tokens_new][head_dim]

@@ -47,6 +47,12 @@ nvfp4_status_t check_matrix(int64_t rows, int64_t k, bool rows_may_be_zero) {
 
 nvfp4_status_t from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
 
+// flags of the quantizing calls: a scale mode, optionally | NVFP4_FOUR_OVER_SIX.
+bool valid_flags(int flags, bool four_over_six_allowed) {
+  const int extra = four_over_six_allowed ? NVFP4_FOUR_OVER_SIX : 0;
+  return (flags & ~(NVFP4_SCALE_GIVEN | extra)) == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,42 +84,44 @@ nvfp4_status_t nvfp4_global_scale(const void* x, nvfp4_dtype_t dtype, int64_t ro
 nvfp4_status_t nvfp4_quantize(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
                               float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
-  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  if (!valid_flags(flags, true)) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_matrix(rows, k, true);
   if (st != NVFP4_OK) return st;
   if (!s_g || (rows > 0 && (!x || !codes || !scales))) return NVFP4_ERR_NULL;
   if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const int64_t units = rows * k / 8;
-  if (flags == NVFP4_SCALE_COMPUTE) {
+  if (!(flags & NVFP4_SCALE_GIVEN)) {
     st = from_hip(nvfp4::launch_global_scale(x, dtype, units, 1, reinterpret_cast<uint32_t*>(codes), units, s_g, s));
     if (st != NVFP4_OK) return st;
   }
-  return from_hip(nvfp4::launch_encode(x, dtype, units, 1, s_g, reinterpret_cast<uint32_t*>(codes), scales, s));
+  return from_hip(nvfp4::launch_encode(x, dtype, units, 1, s_g, reinterpret_cast<uint32_t*>(codes), scales, s, -1, 0,
+                                       (flags & NVFP4_FOUR_OVER_SIX) != 0));
 }
 
 nvfp4_status_t nvfp4_quantize_transposed(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols, uint8_t* codes_t,
                                          uint8_t* scales_t, float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
-  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  if (!valid_flags(flags, true)) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_matrix(cols, rows, true);  // x^T is [cols][rows], blocks along rows
   if (st != NVFP4_OK) return st;
   if (!s_g || (cols > 0 && (!x || !codes_t || !scales_t))) return NVFP4_ERR_NULL;
   if (!aligned(s_g, 4) || !aligned(x, 16) || !aligned(codes_t, 16) || !aligned(scales_t, 4)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const int64_t units = rows * cols / 8;
-  if (flags == NVFP4_SCALE_COMPUTE) {
+  if (!(flags & NVFP4_SCALE_GIVEN)) {
     st = from_hip(nvfp4::launch_global_scale(x, dtype, units, 1, reinterpret_cast<uint32_t*>(codes_t), units, s_g, s));
     if (st != NVFP4_OK) return st;
   }
-  return from_hip(nvfp4::launch_encode_t(x, dtype, rows, cols, s_g, reinterpret_cast<uint32_t*>(codes_t), scales_t, s));
+  return from_hip(nvfp4::launch_encode_t(x, dtype, rows, cols, s_g, reinterpret_cast<uint32_t*>(codes_t), scales_t, s,
+                                         (flags & NVFP4_FOUR_OVER_SIX) != 0));
 }
 
 nvfp4_status_t nvfp4_adaln_quantize(const void* x, nvfp4_dtype_t dtype, int64_t rows, int64_t k, const float* shift,
                                     const float* scale, int64_t rows_per_group, float eps, uint8_t* codes,
                                     uint8_t* scales, float* s_g, int flags, void* stream) {
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
-  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  if (!valid_flags(flags, false)) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_matrix(rows, k, true);
   if (st != NVFP4_OK) return st;
   // one workgroup per 4 rows: the grid and the partial count stay below 2^31
@@ -168,19 +176,20 @@ nvfp4_status_t nvfp4_gemm_fused_act(const void* a, nvfp4_dtype_t a_dtype, int64_
                                     const uint8_t* b_scales, const float* b_sg, int64_t N, void* c,
                                     nvfp4_dtype_t c_dtype, int flags, void* stream) {
   if (!valid_dtype(a_dtype)) return NVFP4_ERR_DTYPE;
-  if (flags != NVFP4_SCALE_COMPUTE && flags != NVFP4_SCALE_GIVEN) return NVFP4_ERR_FLAGS;
+  if (!valid_flags(flags, true)) return NVFP4_ERR_FLAGS;
   nvfp4_status_t st = check_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype);
   if (st != NVFP4_OK) return st;
   if (!a) return NVFP4_ERR_NULL;
   if (!aligned(a, 16)) return NVFP4_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const int64_t units = M * K / 8;
-  if (flags == NVFP4_SCALE_COMPUTE) {
+  if (!(flags & NVFP4_SCALE_GIVEN)) {
     st = from_hip(
         nvfp4::launch_global_scale(a, a_dtype, units, 1, reinterpret_cast<uint32_t*>(a_codes), units, a_sg, s));
     if (st != NVFP4_OK) return st;
   }
-  st = from_hip(nvfp4::launch_encode(a, a_dtype, units, 1, a_sg, reinterpret_cast<uint32_t*>(a_codes), a_scales, s));
+  st = from_hip(nvfp4::launch_encode(a, a_dtype, units, 1, a_sg, reinterpret_cast<uint32_t*>(a_codes), a_scales, s,
+                                     -1, 0, (flags & NVFP4_FOUR_OVER_SIX) != 0));
   if (st != NVFP4_OK) return st;
   return from_hip(nvfp4::launch_gemm(a_codes, a_scales, a_sg, b_codes, b_scales, b_sg, M, N, K, c, c_dtype, s));
 }
@@ -192,8 +201,9 @@ static nvfp4_status_t check_kv(int64_t heads, int64_t tokens, int64_t head_dim) 
   return NVFP4_OK;
 }
 
-nvfp4_status_t kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim, uint8_t* codes,
-                           uint8_t* scales, float* head_scales, void* stream) {
+static nvfp4_status_t kv_quantize_impl(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                                       uint8_t* codes, uint8_t* scales, float* head_scales, bool four_over_six,
+                                       void* stream) {
   nvfp4_status_t st = check_kv(heads, tokens, head_dim);
   if (st != NVFP4_OK) return st;
   if (!head_scales || (tokens > 0 && (!kv || !codes || !scales))) return NVFP4_ERR_NULL;
@@ -205,7 +215,17 @@ nvfp4_status_t kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_
                                            reinterpret_cast<uint32_t*>(codes), units * heads, head_scales, s));
   if (st != NVFP4_OK) return st;
   return from_hip(nvfp4::launch_encode(kv, nvfp4::kDtypeBf16, units, (int)heads, head_scales,
-                                       reinterpret_cast<uint32_t*>(codes), scales, s));
+                                       reinterpret_cast<uint32_t*>(codes), scales, s, -1, 0, four_over_six));
+}
+
+nvfp4_status_t kv_quantize(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim, uint8_t* codes,
+                           uint8_t* scales, float* head_scales, void* stream) {
+  return kv_quantize_impl(kv, heads, tokens, head_dim, codes, scales, head_scales, false, stream);
+}
+
+nvfp4_status_t kv_quantize_four_over_six(const void* kv, int64_t heads, int64_t tokens, int64_t head_dim,
+                                         uint8_t* codes, uint8_t* scales, float* head_scales, void* stream) {
+  return kv_quantize_impl(kv, heads, tokens, head_dim, codes, scales, head_scales, true, stream);
 }
 
 nvfp4_status_t kv_quantize_append(const void* kv_new, int64_t heads, int64_t tokens_new, int64_t head_dim,

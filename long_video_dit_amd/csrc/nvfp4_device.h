@@ -101,7 +101,10 @@ __device__ __forceinline__ float pair_max(float v) {
 struct EncodeConsts {
   float s_g;
   float i6_lo, i6_hi;  // bracket of 1 / (6 s_g)
+  float i4_lo, i4_hi;  // bracket of 1 / (4 s_g) (FourOverSix's second candidate)
   float inv_g;         // ~1 / s_g (within 2^-23)
+  float g_norm;        // s_g 2^-g_exp, in [1, 2) (exact)
+  int g_exp;
   int mode;            // 0 fast, 1 all-zero scale (s_g == 0), 2 exact slow path
 };
 
@@ -110,13 +113,20 @@ __device__ __forceinline__ EncodeConsts make_encode_consts(float s_g) {
   c.s_g = s_g;
   if (!(s_g > 0.0f)) {
     c.mode = 1;
-    c.i6_lo = c.i6_hi = c.inv_g = 0.0f;
+    c.i6_lo = c.i6_hi = c.i4_lo = c.i4_hi = c.inv_g = c.g_norm = 0.0f;
+    c.g_exp = 0;
     return c;
   }
+  int e;
+  (void)__builtin_frexpf(s_g, &e);  // s_g = m 2^e, m in [0.5, 1)
+  c.g_exp = e - 1;
+  c.g_norm = __builtin_ldexpf(s_g, -c.g_exp);
   c.mode = (s_g < kTinyScale) ? 2 : 0;
-  const double i6 = 1.0 / (6.0 * (double)s_g);
+  const double i6 = 1.0 / (6.0 * (double)s_g), i4 = 1.0 / (4.0 * (double)s_g);
   c.i6_lo = (float)(i6 * (double)kBracketLo);
   c.i6_hi = (float)(i6 * (double)kBracketHi);
+  c.i4_lo = (float)(i4 * (double)kBracketLo);
+  c.i4_hi = (float)(i4 * (double)kBracketHi);
   c.inv_g = (float)(1.0 / (double)s_g);
   return c;
 }
@@ -182,6 +192,203 @@ __device__ __forceinline__ uint32_t encode8(const float (&f)[8], uint32_t sb, co
     w |= code << (4 * i);
   }
   return w;
+}
+
+// ---- FourOverSix block scaling ----------------------------------------------
+//
+// Per block, the usual scale byte (block maximum -> 6) or the one that maps the
+// block maximum to 4, whichever dequantizes with the smaller sum of squared
+// errors (equal errors keep the usual one); a reading of the FourOverSix backend
+// the pages name without defining it.
+
+// Exact choice between adjacent scale bytes lo < hi for amax_b / (4 s_g), as
+// scale_pick does for 6: midpoint * 4 has <= 6 significant bits.
+__device__ __forceinline__ uint32_t scale_pick4(float amax_b, float s_g, uint32_t lo, uint32_t hi) {
+  const float mid4 = (e4m3_value(lo) + e4m3_value(hi)) * 2.0f;
+  const double d = __builtin_fma(-(double)mid4, (double)s_g, (double)amax_b);
+  return d > 0.0 ? hi : (d < 0.0 ? lo : ((lo & 1u) ? hi : lo));
+}
+
+__device__ __noinline__ uint32_t scale4_resolve(float amax_b, float s_g, uint32_t c) {
+  if (c < 0x7Eu && scale_pick4(amax_b, s_g, c, c + 1) == c + 1) return c + 1;
+  if (c > 0u && scale_pick4(amax_b, s_g, c - 1, c) == c - 1) return c - 1;
+  return c;
+}
+
+// RNE_SAT_E4M3(amax_b / (4 s_g)), bracketed like encode_scale.
+__device__ __forceinline__ uint32_t encode_scale4(float amax_b, const EncodeConsts& c) {
+  if (c.mode == 1) return 0u;
+  if (c.mode == 2) {
+    const double r = (double)amax_b / (4.0 * (double)c.s_g);
+    return scale4_resolve(amax_b, c.s_g, e4m3_rne_sat((float)r));
+  }
+  const uint32_t lo = e4m3_rne_sat(amax_b * c.i4_lo);
+  const uint32_t hi = e4m3_rne_sat(amax_b * c.i4_hi);
+  return lo == hi ? lo : scale_pick4(amax_b, c.s_g, lo, hi);
+}
+
+// acc + sum over 8 elements of (x - val(code) sv s_g)^2 in fp64.  val(code) sv
+// is exact in fp32 (<= 6 significant bits) and its product with s_g exact in
+// fp64; for the values of one block the difference spans well under 53 bits,
+// so each d is exact and only the squares and the sum round.
+__device__ __forceinline__ double sq_err8(const float (&f)[8], uint32_t w, float sv, double g, double acc) {
+  f32x2 v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const double d0 = __builtin_fma(-(double)(v[j].x * sv), g, (double)f[2 * j]);
+    const double d1 = __builtin_fma(-(double)(v[j].y * sv), g, (double)f[2 * j + 1]);
+    acc = __builtin_fma(d0, d0, acc);
+    acc = __builtin_fma(d1, d1, acc);
+  }
+  return acc;
+}
+
+// Integer significand m and the exponent of its lowest bit, v = m 2^e exactly
+// (m odd, or 0 for v == 0), for a finite double.
+__device__ __forceinline__ void split_dyadic(double v, int64_t& m, int& e) {
+  const uint64_t b = (uint64_t)__builtin_bit_cast(int64_t, v);
+  const int be = (int)((b >> 52) & 0x7ff);
+  uint64_t mant = b & ((uint64_t(1) << 52) - 1);
+  if (be) mant |= uint64_t(1) << 52;
+  if (!mant) {
+    m = 0;
+    e = 0;
+    return;
+  }
+  const int tz = __builtin_ctzll(mant);
+  m = (int64_t)(mant >> tz);
+  e = (be ? be - 1075 : -1074) + tz;
+  if (b >> 63) m = -m;
+}
+
+// Exact sign of E4 - E6 for the 16 values of a block, the candidates' values
+// y = p s_g (p exact fp32 products, s_g fp32): only elements whose two values
+// differ contribute; over them every value is an integer multiple of 2^lo, and
+// (x - y4)^2 - (x - y6)^2 = (y6 - y4)(2x - y4 - y6) is summed in 128-bit
+// integers (the values of one block span < 40 bits, far inside that).
+__device__ __noinline__ int sq_err_sign_exact(const float* x, const float* p4, const float* p6, float s_g) {
+  const double g = (double)s_g;
+  int lo = 0x7fffffff;
+  for (int i = 0; i < 16; i++) {
+    const double y4 = (double)p4[i] * g, y6 = (double)p6[i] * g;
+    if (y4 == y6) continue;
+    const double v[3] = {(double)x[i], y4, y6};
+    for (int j = 0; j < 3; j++) {
+      int64_t m;
+      int e;
+      split_dyadic(v[j], m, e);
+      if (m && e < lo) lo = e;
+    }
+  }
+  if (lo == 0x7fffffff) return 0;
+  __int128 acc = 0;
+  for (int i = 0; i < 16; i++) {
+    const double y4 = (double)p4[i] * g, y6 = (double)p6[i] * g;
+    if (y4 == y6) continue;
+    const double v[3] = {(double)x[i], y4, y6};
+    __int128 n[3];
+    for (int j = 0; j < 3; j++) {
+      int64_t m;
+      int e;
+      split_dyadic(v[j], m, e);
+      n[j] = m ? (__int128)m << (e - lo) : (__int128)0;
+    }
+    acc += (n[2] - n[1]) * (2 * n[0] - n[1] - n[2]);
+  }
+  return acc > 0 ? 1 : (acc < 0 ? -1 : 0);
+}
+
+// Values val(code) sv of the 8 codes of w (exact fp32).
+__device__ __forceinline__ void decode8(uint32_t w, float sv, float* p) {
+  f32x2 v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    p[2 * j] = v[j].x * sv;
+    p[2 * j + 1] = v[j].y * sv;
+  }
+}
+
+__device__ __noinline__ bool prefer4_exact(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
+                                           float v6, uint32_t w4a, uint32_t w4b, float v4, float s_g) {
+  float x[16], p4[16], p6[16];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    x[i] = f0[i];
+    x[8 + i] = f1[i];
+  }
+  decode8(w4a, v4, p4);
+  decode8(w4b, v4, p4 + 8);
+  decode8(w6a, v6, p6);
+  decode8(w6b, v6, p6 + 8);
+  return sq_err_sign_exact(x, p4, p6, s_g) < 0;
+}
+
+// The fp64 comparison: the sums carry at most ~2^-48 relative error, so a
+// difference beyond 2^-44 of their sum decides; nearer (exact ties included)
+// the integer comparison does.
+__device__ __noinline__ bool prefer4_f64(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
+                                         float v6, uint32_t w4a, uint32_t w4b, float v4, float s_g) {
+  const double g = (double)s_g;
+  const double e6 = sq_err8(f1, w6b, v6, g, sq_err8(f0, w6a, v6, g, 0.0));
+  if (e6 == 0.0) return false;  // the usual scale is exact: nothing does better
+  const double e4 = sq_err8(f1, w4b, v4, g, sq_err8(f0, w4a, v4, g, 0.0));
+  const double diff = e6 - e4, tol = 0x1p-44 * (e6 + e4);
+  if (diff > tol) return true;
+  if (diff < -tol) return false;
+  return prefer4_exact(f0, f1, w6a, w6b, v6, w4a, w4b, v4, s_g);
+}
+
+// acc + sum over 8 elements of (xs - val(code) sv gn)^2 in fp32, xs = x 2^-g_exp
+// and gn = s_g 2^-g_exp (both exact): each difference is one rounding of the
+// exact one (fma), each step of the sum one more.
+__device__ __forceinline__ float sq_err8_f32(const float* xs, uint32_t w, float sv, float gn, float acc) {
+  f32x2 v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const float d0 = __builtin_fmaf(-(v[j].x * sv), gn, xs[2 * j]);
+    const float d1 = __builtin_fmaf(-(v[j].y * sv), gn, xs[2 * j + 1]);
+    acc = __builtin_fmaf(d0, d0, acc);
+    acc = __builtin_fmaf(d1, d1, acc);
+  }
+  return acc;
+}
+
+// True when the block (f0, f1) encoded under scale byte sb4 (codes w4a, w4b)
+// has a smaller squared error than under the usual sb6 (codes w6a, w6b).
+// First in fp32 on the block scaled by 2^-g_exp (exact; a block whose two
+// candidates differ lies below ~2600 s_g, so nothing overflows): each sum is
+// within 18 2^-24 of its exact value, so a difference beyond 2^-16 of their sum
+// decides, provided the sums are far from the fp32 subnormal range.  Otherwise
+// (near-ties, exact ties, sums of zero) the fp64 comparison decides.
+__device__ __forceinline__ bool prefer4(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
+                                        uint32_t sb6, uint32_t w4a, uint32_t w4b, uint32_t sb4, const EncodeConsts& c) {
+  const float v6 = e4m3_value(sb6), v4 = e4m3_value(sb4);
+  float xs[16];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    xs[i] = __builtin_ldexpf(f0[i], -c.g_exp);
+    xs[8 + i] = __builtin_ldexpf(f1[i], -c.g_exp);
+  }
+  const float e6 = sq_err8_f32(xs + 8, w6b, v6, c.g_norm, sq_err8_f32(xs, w6a, v6, c.g_norm, 0.0f));
+  const float e4 = sq_err8_f32(xs + 8, w4b, v4, c.g_norm, sq_err8_f32(xs, w4a, v4, c.g_norm, 0.0f));
+  const float sum = e6 + e4, diff = e6 - e4, tol = 0x1p-16f * sum;
+  if (__builtin_expect(sum >= 0x1p-100f, 1)) {
+    if (diff > tol) return true;
+    if (diff < -tol) return false;
+  }
+  return prefer4_f64(f0, f1, w6a, w6b, v6, w4a, w4b, v4, c.s_g);
 }
 
 // RN_bf16 of the exact product p * s_g, where p = val(code) * val(scale) is

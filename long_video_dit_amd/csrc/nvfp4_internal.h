@@ -56,13 +56,13 @@ hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, flo
 // Encode pass; group g is written at unit g * out_group_stride + out_offset
 // (out_group_stride < 0: = units_per_group, a dense tensor).  units_per_group,
 // out_group_stride and out_offset must be even (whole 16-element blocks), else
-// hipErrorInvalidValue.
+// hipErrorInvalidValue.  four_over_six: FourOverSix block scaling.
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
                          uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride = -1,
-                         int64_t out_offset = 0);
+                         int64_t out_offset = 0, bool four_over_six = false);
 // Encode pass along rows: x [rows][cols] -> NVFP4 of x^T (rows % 16 == 0).
 hipError_t launch_encode_t(const void* x, int dtype, int64_t rows, int64_t cols, const float* s_g, uint32_t* codes,
-                           uint8_t* scales, hipStream_t stream);
+                           uint8_t* scales, hipStream_t stream, bool four_over_six = false);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,
                           int groups, void* y, int y_dtype, hipStream_t stream);
 

@@ -10,7 +10,8 @@
 //   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
 //   amax_slot_kernel     standalone s_g: atomic max into the s_g slot itself
-//   encode_kernel        pass 2: scale byte per 16, 8 codes per lane
+//   encode_kernel        pass 2: scale byte per 16, 8 codes per lane (optionally
+//                        FourOverSix: the better of two candidate scales per block)
 //   encode_t_kernel      pass 2 along the other axis: NVFP4 of x^T
 //   dequant_kernel       codes + scales -> bf16 / fp32, 8 outputs per lane
 //
@@ -191,7 +192,29 @@ struct Raw8<float> {
 // block's scale byte.  The loads of the next block are issued before the
 // current one is encoded; their indexes are clamped to the last block
 // (always in bounds) and the stores need no predicate.
-template <typename T>
+// The scale byte and the two code words of one 16-element block: the usual
+// encoding, or with k46 (FourOverSix) the one of the two candidate scales that
+// dequantizes with the smaller squared error.
+template <bool k46>
+__device__ __forceinline__ void encode_block(const float (&f0)[8], const float (&f1)[8], float am, const EncodeConsts& c,
+                                             uint32_t& sb, uint32_t& w0, uint32_t& w1) {
+  sb = encode_scale(am, c);
+  w0 = encode8(f0, sb, c);
+  w1 = encode8(f1, sb, c);
+  if constexpr (k46) {
+    const uint32_t sb4 = encode_scale4(am, c);
+    if (sb4 != sb) {
+      const uint32_t x0 = encode8(f0, sb4, c), x1 = encode8(f1, sb4, c);
+      if (prefer4(f0, f1, w0, w1, sb, x0, x1, sb4, c)) {
+        sb = sb4;
+        w0 = x0;
+        w1 = x1;
+      }
+    }
+  }
+}
+
+template <typename T, bool k46>
 __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int64_t nb, int64_t b0, int64_t stride,
                                                    const EncodeConsts& c, uint32_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales, int64_t base) {
@@ -214,9 +237,8 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
 #pragma unroll
     for (int i = 0; i < 8; i++)
       am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(f0[i]), __builtin_fabsf(f1[i])));
-    const uint32_t sb = encode_scale(am, c);
-    const uint32_t w0 = encode8(f0, sb, c);
-    const uint32_t w1 = encode8(f1, sb, c);
+    uint32_t sb, w0, w1;
+    encode_block<k46>(f0, f1, am, c, sb, w0, w1);
     __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(codes + base) + bk);
     scales[(base >> 1) + bk] = (uint8_t)sb;
   }
@@ -230,7 +252,8 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
 // are even (whole blocks), so the 8-byte code stores stay aligned.  The
 // common case (an ordinary per-tensor scale) runs a copy of the loop in which
 // the encoder's mode is the constant 0, so that no mode test is left inside.
-template <typename T>
+// k46: FourOverSix block scaling.
+template <typename T, bool k46>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, int64_t units_per_group,
                                                           const float* __restrict__ s_g,
                                                           uint32_t* __restrict__ codes,
@@ -246,9 +269,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   if (c.mode == 0) {
     EncodeConsts cf = c;
     cf.mode = 0;
-    encode_lane_blocks(xg, nb, b0, stride, cf, codes, scales, base);
+    encode_lane_blocks<T, k46>(xg, nb, b0, stride, cf, codes, scales, base);
   } else {
-    encode_lane_blocks(xg, nb, b0, stride, c, codes, scales, base);
+    encode_lane_blocks<T, k46>(xg, nb, b0, stride, c, codes, scales, base);
   }
 }
 
@@ -333,7 +356,7 @@ __device__ __forceinline__ void load4<float>(const float* __restrict__ p, float 
 __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
-template <typename T, bool kVec>
+template <typename T, bool kVec, bool k46>
 __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                             const float* __restrict__ s_g,
                                                             uint32_t* __restrict__ codes,
@@ -367,14 +390,15 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
       float am = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; i++) am = __builtin_fmaxf(am, __builtin_fabsf(f[j][i]));
-      const uint32_t sb = encode_scale(am, c);
       float lo[8], hi[8];
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         lo[i] = f[j][i];
         hi[i] = f[j][8 + i];
       }
-      *reinterpret_cast<u32x2*>(&sc[4 * c4 + j][2 * rb]) = u32x2{encode8(lo, sb, c), encode8(hi, sb, c)};
+      uint32_t sb, w0, w1;
+      encode_block<k46>(lo, hi, am, c, sb, w0, w1);
+      *reinterpret_cast<u32x2*>(&sc[4 * c4 + j][2 * rb]) = u32x2{w0, w1};
       reinterpret_cast<uint8_t*>(ss[4 * c4 + j])[rb] = (uint8_t)sb;
     }
   }
@@ -472,7 +496,7 @@ hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, flo
 
 hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int groups, const float* s_g,
                          uint32_t* codes, uint8_t* scales, hipStream_t stream, int64_t out_group_stride,
-                         int64_t out_offset) {
+                         int64_t out_offset, bool four_over_six) {
   if (units_per_group == 0) return hipSuccess;
   if (out_group_stride < 0) out_group_stride = units_per_group;
   // whole blocks: the kernel stores 8 bytes of codes per block
@@ -483,28 +507,34 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
   // block per thread was slower than three
   const int bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
   const dim3 grid((unsigned)bx, (unsigned)groups);
+  auto go = [&](auto kernel, const auto* xt) {
+    return launch_kernel(kernel, grid, dim3(kThreads), 0, stream, xt, units_per_group, s_g, codes, scales,
+                         out_group_stride, out_offset);
+  };
   if (dtype == kDtypeF32)
-    return launch_kernel(encode_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)x, units_per_group, s_g,
-                         codes, scales, out_group_stride, out_offset);
-  return launch_kernel(encode_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, units_per_group,
-                       s_g, codes, scales, out_group_stride, out_offset);
+    return four_over_six ? go(encode_kernel<float, true>, (const float*)x) : go(encode_kernel<float, false>, (const float*)x);
+  return four_over_six ? go(encode_kernel<uint16_t, true>, (const uint16_t*)x)
+                       : go(encode_kernel<uint16_t, false>, (const uint16_t*)x);
 }
 
 hipError_t launch_encode_t(const void* x, int dtype, int64_t rows, int64_t cols, const float* s_g, uint32_t* codes,
-                           uint8_t* scales, hipStream_t stream) {
+                           uint8_t* scales, hipStream_t stream, bool four_over_six) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const int64_t tiles = (rows + kTR - 1) / kTR * ((cols + kTC - 1) / kTC);
   const dim3 grid((unsigned)tiles);
   const bool vec = cols % 4 == 0;
-  if (dtype == kDtypeF32)
-    return vec ? launch_kernel(encode_t_kernel<float, true>, grid, dim3(kTThreads), 0, stream, (const float*)x, rows,
-                               cols, s_g, codes, scales)
-               : launch_kernel(encode_t_kernel<float, false>, grid, dim3(kTThreads), 0, stream, (const float*)x, rows,
-                               cols, s_g, codes, scales);
-  return vec ? launch_kernel(encode_t_kernel<uint16_t, true>, grid, dim3(kTThreads), 0, stream, (const uint16_t*)x,
-                             rows, cols, s_g, codes, scales)
-             : launch_kernel(encode_t_kernel<uint16_t, false>, grid, dim3(kTThreads), 0, stream, (const uint16_t*)x,
-                             rows, cols, s_g, codes, scales);
+  auto go = [&](auto kernel, const auto* xt) {
+    return launch_kernel(kernel, grid, dim3(kTThreads), 0, stream, xt, rows, cols, s_g, codes, scales);
+  };
+  const float* xf = (const float*)x;
+  const uint16_t* xb = (const uint16_t*)x;
+  if (dtype == kDtypeF32) {
+    if (four_over_six) return vec ? go(encode_t_kernel<float, true, true>, xf) : go(encode_t_kernel<float, false, true>, xf);
+    return vec ? go(encode_t_kernel<float, true, false>, xf) : go(encode_t_kernel<float, false, false>, xf);
+  }
+  if (four_over_six)
+    return vec ? go(encode_t_kernel<uint16_t, true, true>, xb) : go(encode_t_kernel<uint16_t, false, true>, xb);
+  return vec ? go(encode_t_kernel<uint16_t, true, false>, xb) : go(encode_t_kernel<uint16_t, false, false>, xb);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* s_g, int64_t blocks_per_group,

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_LAUNCH, ERR_FLAGS = range(7)
 F32, BF16 = 0, 1
 SCALE_COMPUTE, SCALE_GIVEN = 0, 1
+FOUR_OVER_SIX = 2  # flag bit: FourOverSix block scaling
 
 # Exported names and C signatures, in the order include/nvfp4.h declares them
 # (C enums are passed as int).
@@ -36,6 +37,7 @@ SIGNATURES = {
     "nvfp4_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemm_fused_act": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _I, _I, _P]),
     "kv_quantize": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "kv_quantize_four_over_six": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "kv_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _I64, _P]),
     "kv_rope_quantize_append": (_I, [_P, _I64, _I64, _I64, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _P]),
     "kv_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
@@ -195,12 +197,13 @@ def _slot_or_new(t, device):
     return torch.empty(1, dtype=torch.float32, device=device) if t is None else t
 
 
-def quantize(x, s_g=None, out=None, s_g_out=None):
+def quantize(x, s_g=None, out=None, s_g_out=None, four_over_six=False):
     """x [rows, k] (float32/bfloat16, device) -> (codes u8 [rows, k/2], scales u8 [rows, k/16], s_g f32 [1]).
 
     With s_g given (a device tensor [1]) it is used as is (NVFP4_SCALE_GIVEN);
     otherwise it is computed into s_g_out (allocated when None).  `out` may
-    pass preallocated (codes, scales)."""
+    pass preallocated (codes, scales).  four_over_six: FourOverSix block scaling
+    (NVFP4_FOUR_OVER_SIX)."""
     ops = _Operands()
     rows, k = ops.dims(x, "x", 2)
     ops.want(x, "x", (rows, k), _FLOATS)
@@ -210,14 +213,16 @@ def quantize(x, s_g=None, out=None, s_g_out=None):
     dev = ops.device()
     codes, scales = _alloc_packed(rows, k, out, dev)
     s_g = _slot_or_new(s_g, dev)
+    if four_over_six:
+        flags |= FOUR_OVER_SIX
     _call("nvfp4_quantize", _ptr(x), _dt(x), rows, k, _ptr(codes), _ptr(scales), _ptr(s_g), flags, _stream(dev))
     return codes, scales, s_g
 
 
-def quantize_transposed(x, s_g=None, out=None, s_g_out=None):
+def quantize_transposed(x, s_g=None, out=None, s_g_out=None, four_over_six=False):
     """x [rows, cols] (float32/bfloat16, device) quantized along its rows: the NVFP4 form of x.T,
     (codes u8 [cols, rows/2], scales u8 [cols, rows/16], s_g f32 [1]), without a transposed copy.
-    s_g, out and s_g_out as in quantize."""
+    s_g, out, s_g_out and four_over_six as in quantize."""
     ops = _Operands()
     rows, cols = ops.dims(x, "x", 2)
     ops.want(x, "x", (rows, cols), _FLOATS)
@@ -227,6 +232,8 @@ def quantize_transposed(x, s_g=None, out=None, s_g_out=None):
     dev = ops.device()
     codes, scales = _alloc_packed(cols, rows, out, dev)
     s_g = _slot_or_new(s_g, dev)
+    if four_over_six:
+        flags |= FOUR_OVER_SIX
     _call("nvfp4_quantize_transposed", _ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(s_g), flags,
           _stream(dev))
     return codes, scales, s_g
@@ -312,12 +319,13 @@ def gemm(a, b, out_dtype=torch.bfloat16, out=None):
     return c
 
 
-def gemm_fused_act(a, b, out_dtype=torch.bfloat16, out=None, a_q=None, s_g=None):
+def gemm_fused_act(a, b, out_dtype=torch.bfloat16, out=None, a_q=None, s_g=None, four_over_six=False):
     """Quantize activations a [M, K] and compute C = A_q . B^T.
 
     s_g: a device tensor [1] holding the activation scale (e.g. from global_scale), used as
     given (NVFP4_SCALE_GIVEN); None computes it from a.  a_q may pass preallocated
-    (codes, scales[, s_g_out]) for the packed activation.  Returns (C, (codes, scales, s_g))."""
+    (codes, scales[, s_g_out]) for the packed activation.  four_over_six: FourOverSix block
+    scaling of the activation.  Returns (C, (codes, scales, s_g))."""
     ops = _Operands()
     M, K = ops.dims(a, "a", 2)
     ops.want(a, "a", (M, K), _FLOATS)
@@ -333,13 +341,16 @@ def gemm_fused_act(a, b, out_dtype=torch.bfloat16, out=None, a_q=None, s_g=None)
     sg = _slot_or_new(sg, dev)
     c = torch.empty(M, N, dtype=out_dtype, device=dev) if out is None else out
     bc, bs, bg = b[:3]
+    if four_over_six:
+        flags |= FOUR_OVER_SIX
     _call("nvfp4_gemm_fused_act", _ptr(a), _dt(a), M, K, _ptr(sg), _ptr(codes), _ptr(scales), _ptr(bc),
           _ptr(bs), _ptr(bg), N, _ptr(c), _dt(c), flags, _stream(dev))
     return c, (codes, scales, sg)
 
 
-def kv_quantize(kv, out=None):
-    """kv bf16 [H, T, D] -> (codes [H, T, D/2], scales [H, T, D/16], head_scales f32 [H])."""
+def kv_quantize(kv, out=None, four_over_six=False):
+    """kv bf16 [H, T, D] -> (codes [H, T, D/2], scales [H, T, D/16], head_scales f32 [H]);
+    four_over_six: FourOverSix block scaling (kv_quantize_four_over_six)."""
     ops = _Operands()
     H, T, D = ops.dims(kv, "kv", 3)
     ops.want(kv, "kv", (H, T, D), _BF16)
@@ -351,7 +362,8 @@ def kv_quantize(kv, out=None):
         out = (torch.empty(H, T, D // 2, dtype=torch.uint8, device=dev),
                torch.empty(H, T, D // 16, dtype=torch.uint8, device=dev),
                torch.empty(H, dtype=torch.float32, device=dev))
-    _call("kv_quantize", _ptr(kv), H, T, D, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _stream(dev))
+    _call("kv_quantize_four_over_six" if four_over_six else "kv_quantize", _ptr(kv), H, T, D, _ptr(out[0]),
+          _ptr(out[1]), _ptr(out[2]), _stream(dev))
     return out
 
 

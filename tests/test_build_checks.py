@@ -59,6 +59,8 @@ def test_validation_errors_launch_nothing():
     # quantize
     assert lib.nvfp4_quantize(buf, 7, 4, 32, buf, buf, buf, 0, None) == nv.ERR_DTYPE
     assert lib.nvfp4_quantize(buf, 1, 4, 32, buf, buf, buf, 5, None) == nv.ERR_FLAGS
+    assert lib.nvfp4_quantize(buf, 1, 4, 32, buf, buf, buf, 4, None) == nv.ERR_FLAGS
+    assert lib.nvfp4_quantize(buf, 1, 4, 24, buf, buf, buf, 3, None) == nv.ERR_SHAPE  # 4o6 | given: valid flags
     assert lib.nvfp4_quantize(buf, 1, 4, 24, buf, buf, buf, 0, None) == nv.ERR_SHAPE
     assert lib.nvfp4_quantize(buf, 1, -1, 32, buf, buf, buf, 0, None) == nv.ERR_SHAPE
     assert lib.nvfp4_quantize(buf, 1, 4, 0, buf, buf, buf, 0, None) == nv.ERR_SHAPE
@@ -89,7 +91,7 @@ def test_validation_errors_launch_nothing():
     fa = lib.nvfp4_gemm_fused_act
     assert fa(buf, 5, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_DTYPE
     assert fa(buf, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 7, 0, None) == nv.ERR_DTYPE  # c dtype
-    assert fa(buf, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 2, None) == nv.ERR_FLAGS
+    assert fa(buf, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 4, None) == nv.ERR_FLAGS
     assert fa(None, 1, 8, 32, buf, buf, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_NULL
     assert fa(buf, 1, 8, 32, None, buf, buf, buf, buf, buf, 8, buf, 1, 1, None) == nv.ERR_NULL  # a_sg, given
     assert fa(buf, 1, 8, 32, buf, None, buf, buf, buf, buf, 8, buf, 1, 0, None) == nv.ERR_NULL  # a_codes
@@ -156,6 +158,13 @@ def test_validation_errors_launch_nothing():
     assert ad(buf, 1, 4, 64, buf, odd, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_ALIGN
     assert ad(buf, 3, 4, 64, buf, buf, 2, 1e-6, buf, buf, buf, 0, None) == nv.ERR_DTYPE
     assert ad(buf, 1, 4, 64, buf, buf, 2, 1e-6, buf, buf, buf, 9, None) == nv.ERR_FLAGS
+    assert ad(buf, 1, 4, 64, buf, buf, 2, 1e-6, buf, buf, buf, 2, None) == nv.ERR_FLAGS  # no FourOverSix here
+    k46 = lib.kv_quantize_four_over_six
+    assert k46(buf, 0, 16, 128, buf, buf, buf, None) == nv.ERR_SHAPE
+    assert k46(buf, 4, 16, 120, buf, buf, buf, None) == nv.ERR_SHAPE
+    assert k46(buf, 4, 16, 128, buf, buf, None, None) == nv.ERR_NULL
+    assert k46(buf, 4, 16, 128, odd, buf, buf, None) == nv.ERR_ALIGN
+    assert qt(buf, 1, 32, 8, buf, buf, buf, 6, None) == nv.ERR_FLAGS
 
 
 def test_attention_split_choice():
