@@ -359,23 +359,30 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, ui
 
 constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code bytes per row
 
+// The fast path's output tile is 256 rows of A by 64 FN rows of B: each of
+// the 4 waves (2 x 2) holds 128 rows x 32 FN columns, FN = 4 (256 x 256) or
+// FN = 3 (256 x 192, which tiles a 3072-column output into 16 instead of 12
+// columns of tiles).  FN is the number of 32-column B fragments per wave.
+template <int FN>
 struct __attribute__((aligned(16))) FastStage {
-  uint8_t a_codes[kTile * 128];  // [row][8 slots of 16 B], slot = plane q ^ ((row / 2) % 8)
-  uint8_t b_codes[kTile * 128];
-  uint8_t a_scales[kTile * 16];  // [row][16 scale bytes]
-  uint8_t b_scales[kTile * 16];
+  uint8_t a_codes[kTile * 128];    // [row][8 slots of 16 B], slot = plane q ^ ((row / 2) % 8)
+  uint8_t b_codes[64 * FN * 128];  // the same for the 64 FN rows of B
+  uint8_t a_scales[kTile * 16];    // [row][16 scale bytes]
+  uint8_t b_scales[64 * FN * 16];
+  // LDS byte offsets of the parts of a stage.
+  static constexpr uint32_t kA = 0, kB = kTile * 128, kSA = kB + 64 * FN * 128, kSB = kSA + kTile * 16;
 };
-// LDS byte offsets of the parts of a stage.
-constexpr uint32_t kStA = 0, kStB = kTile * 128, kStSA = 2 * kTile * 128, kStSB = 2 * kTile * 128 + kTile * 16;
 
-// Copies of one stage (K = 256 of a 256-row tile of A and of B) issued by one
-// thread: wave w fills rows 64 w .. 64 w + 63 of both operands, 8 rows (1 KiB
-// of codes) per 16-byte copy instruction and all 64 rows of scale bytes (16
-// per row and stage, 16-byte aligned since K % 512 == 0) with one more.  For a full tile the per-lane part of each source offset only
-// depends on the lane and on the instruction's parity (the plane swizzle
-// q ^ ((row / 2) % 8) repeats every 16 rows), so it is kept in 3 VGPRs and
-// the row advance goes into the uniform SGPR base.  Tiles that cross the
-// last row of A or B clamp every lane's row and take the per-lane path.
+// Copies of one stage (K = 256 of the tile's A and B rows) issued by one
+// thread: wave w fills A rows 64 w .. 64 w + 63 and B rows 16 FN w ..
+// 16 FN w + 16 FN - 1, 8 rows (1 KiB of codes) per 16-byte copy instruction,
+// and 64 rows of scale bytes (16 per row and stage, 16-byte aligned since
+// K % 512 == 0) per copy: A's rows 64 w .., B's for the first FN waves.  For
+// a full tile the per-lane part of each source offset only depends on the
+// lane and on the instruction's parity (the plane swizzle q ^ ((row / 2) % 8)
+// repeats every 16 rows), so it is kept in 3 VGPRs and the row advance goes
+// into the uniform SGPR base.  Tiles that cross the last row of A or B clamp
+// every lane's row and take the per-lane path.
 struct FastLoad {
   uint32_t vo[2];  // code offsets of even / odd instructions (full tiles)
   uint32_t vs;     // scale row offset (full tiles)
@@ -396,63 +403,76 @@ __device__ __forceinline__ FastLoad fast_load_offsets(int K) {
 }
 
 // Stage kc of the tile at rows (m0, n0) -> the LDS stage at address `lds`.
+template <int FN>
 __device__ __forceinline__ void fast_load_stage(uint32_t lds, const FastLoad& o, bool edge,
                                                 const uint8_t* __restrict__ a_codes,
                                                 const uint8_t* __restrict__ a_scales,
                                                 const uint8_t* __restrict__ b_codes,
                                                 const uint8_t* __restrict__ b_scales, int64_t m0, int64_t n0, int M,
                                                 int N, int K, int kc) {
+  using S = FastStage<FN>;
+  constexpr int kCopiesB = 2 * FN;  // 8-row copies of B per wave (even: the parity rule above holds)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t row_bytes = K / 2, srow_bytes = K / 16;
   if (!edge) {
     const uint8_t* ac = a_codes + (m0 + 64 * w) * row_bytes + kc * 128;
-    const uint8_t* bc = b_codes + (n0 + 64 * w) * row_bytes + kc * 128;
+    const uint8_t* bc = b_codes + (n0 + 16 * FN * w) * row_bytes + kc * 128;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const uint32_t slot0 = (uint32_t)(w * 8 + i) * 64;
-      lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], lds + kStA + slot0 * 16);
-      lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], lds + kStB + slot0 * 16);
+      lds_dma16(ac + 8 * i * row_bytes, o.vo[i & 1], lds + S::kA + (uint32_t)(w * 8 + i) * 64 * 16);
+      if (i < kCopiesB)
+        lds_dma16(bc + 8 * i * row_bytes, o.vo[i & 1], lds + S::kB + (uint32_t)(w * kCopiesB + i) * 64 * 16);
     }
     const uint32_t d0 = (uint32_t)w * 64 * 16;
-    lds_dma16(a_scales + (m0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + kStSA + d0);
-    lds_dma16(b_scales + (n0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + kStSB + d0);
+    lds_dma16(a_scales + (m0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + S::kSA + d0);
+    if (FN == 4 || w < FN) lds_dma16(b_scales + (n0 + 64 * w) * srow_bytes + kc * 16, o.vs, lds + S::kSB + d0);
     return;
   }
   const uint8_t* ac = a_codes + kc * 128;
   const uint8_t* bc = b_codes + kc * 128;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const int slot0 = (w * 8 + i) * 64;
-    const int row = (slot0 + lane) >> 3;
-    const uint32_t q = ((slot0 + lane) & 7) ^ ((row >> 1) & 7);
-    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
-    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
-    lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, lds + kStA + (uint32_t)slot0 * 16);
-    lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, lds + kStB + (uint32_t)slot0 * 16);
+    {
+      const int slot0 = (w * 8 + i) * 64;
+      const int row = (slot0 + lane) >> 3;
+      const uint32_t q = ((slot0 + lane) & 7) ^ ((row >> 1) & 7);
+      const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+      lds_dma16(ac, (uint32_t)(ra * row_bytes) + 16 * q, lds + S::kA + (uint32_t)slot0 * 16);
+    }
+    if (i < kCopiesB) {
+      const int slot0 = (w * kCopiesB + i) * 64;
+      const int row = (slot0 + lane) >> 3;
+      const uint32_t q = ((slot0 + lane) & 7) ^ ((row >> 1) & 7);
+      const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+      lds_dma16(bc, (uint32_t)(rb * row_bytes) + 16 * q, lds + S::kB + (uint32_t)slot0 * 16);
+    }
   }
   const int row = 64 * w + lane;
   const int64_t ra = m0 + row < M ? m0 + row : M - 1;
-  const int64_t rb = n0 + row < N ? n0 + row : N - 1;
   const uint32_t d0 = (uint32_t)w * 64 * 16;
-  lds_dma16(a_scales + kc * 16, (uint32_t)(ra * srow_bytes), lds + kStSA + d0);
-  lds_dma16(b_scales + kc * 16, (uint32_t)(rb * srow_bytes), lds + kStSB + d0);
+  lds_dma16(a_scales + kc * 16, (uint32_t)(ra * srow_bytes), lds + S::kSA + d0);
+  if (FN == 4 || w < FN) {
+    const int64_t rb = n0 + row < N ? n0 + row : N - 1;
+    lds_dma16(b_scales + kc * 16, (uint32_t)(rb * srow_bytes), lds + S::kSB + d0);
+  }
 }
 
 // Registers that carry the pipeline from step to step: the packed codes and
 // fp16 scale pairs of two sub-chunks (sub-chunk s of a stage uses buffer
 // s % 2) and the decoded MFMA operands of two k16-steps (step parity).
+template <int FN>
 struct FastPipe {
-  uint4 ca[2][4], cb[2][4];
-  uint32_t sa[2][4], sb[2][4];
-  f16x8 av[2][4], bv[2][4];
+  uint4 ca[2][4], cb[2][FN];
+  uint32_t sa[2][4], sb[2][FN];
+  f16x8 av[2][4], bv[2][FN];
 };
 
 // Per-lane LDS offsets of the operand reads: lane (r, h) of wave (wm, wn)
-// reads rows wm * 128 + 32 i + r of A and wn * 128 + 32 j + r of B; within
+// reads rows wm * 128 + 32 i + r of A and wn * 32 FN + 32 j + r of B; within
 // a row, code plane q sits in slot q ^ sw with sw = (r / 2) % 8 (the same
-// for all 4 rows, which are 4 KiB apart), and the scale bytes of blocks 2q,
-// 2q + 1 at byte 2q.
+// for all rows of the lane, which are 4 KiB apart), and the scale bytes of
+// blocks 2q, 2q + 1 at byte 2q.
 struct FastLane {
   uint32_t a, b;    // code row offsets (row * 128) of row i = 0
   uint32_t sa, sb;  // scale byte offsets (row * 16 + 2 h) of row i = 0
@@ -460,13 +480,15 @@ struct FastLane {
 };
 
 // Sub-chunk s (K = 64 s .. 64 s + 63 of a stage) of LDS stage S -> buffer u:
-// this lane's 16 code bytes of plane q = 2 s + h of its 4 A rows and 4 B rows
-// (one 16-byte read each) and the 2 scale bytes of blocks 2q, 2q + 1 of each
-// row, left raw: fast_convert_scales turns them into fp16 once the reads
+// this lane's 16 code bytes of plane q = 2 s + h of its 4 A rows and FN B
+// rows (one 16-byte read each) and the 2 scale bytes of blocks 2q, 2q + 1 of
+// each row, left raw: fast_convert_scales turns them into fp16 once the reads
 // have landed.  The row offsets pass through an empty asm statement so that
 // the compiler derives each address here instead of keeping all of them
 // (2 stages x 4 sub-chunks x 8 rows) live in registers.
-__device__ __forceinline__ void fast_read_sub(const FastStage& S, FastPipe& P, int u, const FastLane& L, int s) {
+template <int FN>
+__device__ __forceinline__ void fast_read_sub(const FastStage<FN>& S, FastPipe<FN>& P, int u, const FastLane& L,
+                                              int s) {
   uint32_t la = L.a, lb = L.b, lsa = L.sa, lsb = L.sb;
   asm volatile("" : "+v"(la), "+v"(lb), "+v"(lsa), "+v"(lsb));
   const uint32_t slot = L.hsw ^ (32u * s);
@@ -478,29 +500,37 @@ __device__ __forceinline__ void fast_read_sub(const FastStage& S, FastPipe& P, i
   for (int i = 0; i < 4; i++) {
     P.ca[u][i] = *reinterpret_cast<const uint4*>(ac + 4096 * i);
     P.sa[u][i] = *reinterpret_cast<const uint16_t*>(as + 512 * i);
-    P.cb[u][i] = *reinterpret_cast<const uint4*>(bc + 4096 * i);
-    P.sb[u][i] = *reinterpret_cast<const uint16_t*>(bs + 512 * i);
+    if (i < FN) {
+      P.cb[u][i] = *reinterpret_cast<const uint4*>(bc + 4096 * i);
+      P.sb[u][i] = *reinterpret_cast<const uint16_t*>(bs + 512 * i);
+    }
   }
 }
 
 // Two E4M3 scale bytes -> two fp16 with the hardware converter (scale 1.0).
 // Exact: every finite E4M3 value, subnormals and signed zero included, is an
 // fp16 value.
-__device__ __forceinline__ void fast_convert_scales(FastPipe& P, int u) {
+template <int FN>
+__device__ __forceinline__ void fast_convert_scales(FastPipe<FN>& P, int u) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     P.sa[u][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P.sa[u][i], 1.0f, false));
-    P.sb[u][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P.sb[u][i], 1.0f, false));
+    if (i < FN)
+      P.sb[u][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P.sb[u][i], 1.0f, false));
   }
 }
 
 // The first k16-step of a workgroup's pipeline (sub-chunk 0, word 0, blocks 2h).
-__device__ __forceinline__ void fast_decode_first(FastPipe& P) {
+template <int FN>
+__device__ __forceinline__ void fast_decode_first(FastPipe<FN>& P) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const _Float16 sa = __builtin_bit_cast(f16x2, P.sa[0][i]).x, sb = __builtin_bit_cast(f16x2, P.sb[0][i]).x;
+    const _Float16 sa = __builtin_bit_cast(f16x2, P.sa[0][i]).x;
     P.av[0][i] = decode8(P.ca[0][i].x, f16x2{sa, sa});
-    P.bv[0][i] = decode8(P.cb[0][i].x, f16x2{sb, sb});
+    if (i < FN) {
+      const _Float16 sb = __builtin_bit_cast(f16x2, P.sb[0][i]).x;
+      P.bv[0][i] = decode8(P.cb[0][i].x, f16x2{sb, sb});
+    }
   }
 }
 
@@ -518,9 +548,6 @@ __device__ __forceinline__ void fast_decode_first(FastPipe& P) {
 #define NVFP4_DEC_PAIR(O, W, S, SEL, OPS)                                          \
   "v_cvt_scalef32_pk_f16_fp4 %[" O "], %[" W "], 1.0" SEL "\n\t"                  \
   "v_pk_mul_f16 %[" O "], %[" S "], %[" O "]" OPS "\n\t"
-#define NVFP4_DEC_FRAG(P, W, S, OPS)                                               \
-  NVFP4_DEC_PAIR(P "0", W, S, "", OPS) NVFP4_DEC_PAIR(P "1", W, S, " op_sel:[1,0,0]", OPS) \
-  NVFP4_DEC_PAIR(P "2", W, S, " op_sel:[0,1,0]", OPS) NVFP4_DEC_PAIR(P "3", W, S, " op_sel:[1,1,0]", OPS)
 #define NVFP4_MFMA(C) "v_mfma_f32_32x32x16_f16 %[" C "], %[b], %[a" C "], %[" C "]\n\t"
 
 template <bool kHi>
@@ -554,14 +581,59 @@ __device__ __forceinline__ void mfma4_decode2(f32x16& c0, f32x16& c1, f32x16& c2
   oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
 }
 
+// The same with three frags (x, y, z) decoded around the 4 MFMAs, 6 decode
+// VALU instructions after each: the last block of a k16-step of a 256 x 192
+// tile, which decodes the next step's 3 B frags.  The hazard rules above
+// hold: the outputs' last MFMA readers are the previous step's blocks, and
+// their first readers come in the next step's blocks, after its s_nop.
+template <bool kHi>
+__device__ __forceinline__ void mfma4_decode3(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const f16x8& b,
+                                              const f16x8 (&a)[4], uint32_t wx, uint32_t sx, uint32_t wy,
+                                              uint32_t sy, uint32_t wz, uint32_t sz, f16x8& ox, f16x8& oy,
+                                              f16x8& oz) {
+  uint32_t x0, x1, x2, x3, y0, y1, y2, y3, z0, z1, z2, z3;
+#define NVFP4_BODY3(OPS)                                                                                  \
+  "s_nop 1\n\t" NVFP4_MFMA("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                                \
+      NVFP4_DEC_PAIR("x1", "wx", "sx", " op_sel:[1,0,0]", OPS)                                            \
+      NVFP4_DEC_PAIR("x2", "wx", "sx", " op_sel:[0,1,0]", OPS) NVFP4_MFMA("c1")                           \
+      NVFP4_DEC_PAIR("x3", "wx", "sx", " op_sel:[1,1,0]", OPS) NVFP4_DEC_PAIR("y0", "wy", "sy", "", OPS)  \
+      NVFP4_DEC_PAIR("y1", "wy", "sy", " op_sel:[1,0,0]", OPS) NVFP4_MFMA("c2")                           \
+      NVFP4_DEC_PAIR("y2", "wy", "sy", " op_sel:[0,1,0]", OPS)                                            \
+      NVFP4_DEC_PAIR("y3", "wy", "sy", " op_sel:[1,1,0]", OPS) NVFP4_DEC_PAIR("z0", "wz", "sz", "", OPS)  \
+      NVFP4_MFMA("c3") NVFP4_DEC_PAIR("z1", "wz", "sz", " op_sel:[1,0,0]", OPS)                           \
+      NVFP4_DEC_PAIR("z2", "wz", "sz", " op_sel:[0,1,0]", OPS) NVFP4_DEC_PAIR("z3", "wz", "sz", " op_sel:[1,1,0]", OPS)
+  if constexpr (kHi) {
+    asm volatile(NVFP4_BODY3(" op_sel:[1,0] op_sel_hi:[1,1]")
+                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
+                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3),
+                   [z0] "=&v"(z0), [z1] "=&v"(z1), [z2] "=&v"(z2), [z3] "=&v"(z3)
+                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
+                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy), [wz] "v"(wz), [sz] "v"(sz));
+  } else {
+    asm volatile(NVFP4_BODY3(" op_sel:[0,0] op_sel_hi:[0,1]")
+                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
+                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3),
+                   [z0] "=&v"(z0), [z1] "=&v"(z1), [z2] "=&v"(z2), [z3] "=&v"(z3)
+                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
+                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy), [wz] "v"(wz), [sz] "v"(sz));
+  }
+#undef NVFP4_BODY3
+  ox = __builtin_bit_cast(f16x8, u32x4{x0, x1, x2, x3});
+  oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
+  oz = __builtin_bit_cast(f16x8, u32x4{z0, z1, z2, z3});
+}
+
 // k16-step n of a stage read from LDS stage S: the codes and scales of
 // sub-chunk s + 1 are read at step 4 s and converted at step 4 s + 2; the
-// step's 16 MFMAs (operands decoded one step earlier) carry the decode of
+// step's 4 FN MFMAs (operands decoded one step earlier) carry the decode of
 // step n + 1, which for n = 15 is the first step of the next stage (its
 // sub-chunk 0 is read in buffer 0 at step 12).  After the last stage of a
-// workgroup that decode works on stale registers and is never used.
-template <int n>
-__device__ __forceinline__ void fast_step(const FastStage& S, FastPipe& P, f32x16 (&acc)[4][4], const FastLane& L) {
+// workgroup that decode works on stale registers and is never used.  With
+// FN = 4 blocks 0-1 decode the next step's A frags and blocks 2-3 its B
+// frags; with FN = 3 block 2 decodes all three B frags.
+template <int n, int FN>
+__device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& P, f32x16 (&acc)[FN][4],
+                                          const FastLane& L) {
   constexpr int s = n >> 2, t = n & 3;
   if constexpr (t == 0 && s < 3) fast_read_sub(S, P, (s + 1) & 1, L, s + 1);
   if constexpr (t == 2 && s < 3) fast_convert_scales(P, (s + 1) & 1);
@@ -570,18 +642,22 @@ __device__ __forceinline__ void fast_step(const FastStage& S, FastPipe& P, f32x1
   // the next step: word t1 of the sub-chunk in buffer u1
   constexpr int t1 = (n + 1) & 3, u1 = n < 15 ? ((n + 1) >> 2) & 1 : 0;
   constexpr bool hi = t1 >= 2;
-  {
-    const uint4* A = P.ca[u1];
-    const uint4* B = P.cb[u1];
-    // blocks 0-1 decode the next step's A frags, blocks 2-3 its B frags
-    mfma4_decode2<hi>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
-                      word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1]);
-    mfma4_decode2<hi>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
-                      word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3]);
+  const uint4* A = P.ca[u1];
+  const uint4* B = P.cb[u1];
+  mfma4_decode2<hi>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
+                    word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1]);
+  mfma4_decode2<hi>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
+                    word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3]);
+  if constexpr (FN == 4) {
     mfma4_decode2<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
                       word_of(B[1], t1), P.sb[u1][1], P.bv[x][0], P.bv[x][1]);
     mfma4_decode2<hi>(acc[3][0], acc[3][1], acc[3][2], acc[3][3], P.bv[c][3], P.av[c], word_of(B[2], t1), P.sb[u1][2],
                       word_of(B[3], t1), P.sb[u1][3], P.bv[x][2], P.bv[x][3]);
+  } else {
+    static_assert(FN == 3, "FN is 3 or 4");
+    mfma4_decode3<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
+                      word_of(B[1], t1), P.sb[u1][1], word_of(B[2], t1), P.sb[u1][2], P.bv[x][0], P.bv[x][1],
+                      P.bv[x][2]);
   }
 }
 
@@ -591,9 +667,9 @@ __device__ __forceinline__ void fast_step(const FastStage& S, FastPipe& P, f32x1
 // issues the copies of the stage after next into S, and sub-chunk 0 of Sn is
 // read for the decode carried by step 15 (after the last stage of a
 // workgroup Sn holds stale data, read but never used).
-template <typename Refill>
-__device__ __forceinline__ void fast_stage(const FastStage& S, const FastStage& Sn, FastPipe& P, f32x16 (&acc)[4][4],
-                                           const FastLane& L, Refill&& refill) {
+template <int FN, typename Refill>
+__device__ __forceinline__ void fast_stage(const FastStage<FN>& S, const FastStage<FN>& Sn, FastPipe<FN>& P,
+                                           f32x16 (&acc)[FN][4], const FastLane& L, Refill&& refill) {
   fast_step<0>(S, P, acc, L);
   fast_step<1>(S, P, acc, L);
   fast_step<2>(S, P, acc, L);
@@ -620,7 +696,7 @@ __device__ __forceinline__ void fast_stage(const FastStage& S, const FastStage& 
 // is output row m = 32 i + r and column n = 32 j + 8 (e / 4) + 4 h + e % 4;
 // one 8-byte (bf16) or 16-byte (fp32) store per 4 consecutive columns.
 // The accumulators of one MFMA tile, read out only where the epilogue uses
-// them.  Without the empty asm the compiler reads all 256 accumulators into
+// them.  Without the empty asm the compiler reads all the accumulators into
 // VGPRs ahead of the full/edge branch (both paths read them), runs out of
 // VGPRs and spills; the reloads then wait, since vmcnt also counts stores,
 // for every output store issued before them.
@@ -643,19 +719,19 @@ __device__ __forceinline__ void fast_store4(void* __restrict__ c, int64_t idx, c
 }
 
 // Tiles that cross row M or column N: every store checks its row and column.
-template <bool kBf16Out>
-__device__ __forceinline__ void fast_epilogue_edge(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+template <bool kBf16Out, int FN>
+__device__ __forceinline__ void fast_epilogue_edge(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
                                                    int64_t n0, int M, int N, int wm, int wn, int r, int h, float g) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int64_t m = m0 + wm * 128 + 32 * i + r;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < FN; j++) {
       const f32x16 a = pinned(acc[j][i]);
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) {
-        const int64_t n = n0 + wn * 128 + 32 * j + 8 * gq + 4 * h;
+        const int64_t n = n0 + wn * 32 * FN + 32 * j + 8 * gq + 4 * h;
         if (n >= N) continue;  // N % 4 == 0: the 4 columns are all in or all out
         fast_store4<kBf16Out>(c, m * N + n, a, gq, g);
       }
@@ -669,55 +745,76 @@ __device__ __forceinline__ uint32_t bf16_pair(const f32x16& a, int gq, int e, fl
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Full tiles of an output with fewer than 2^32 elements, bf16: the output is
-// staged through a wave-private 4 KiB LDS chunk (32 rows x 64 columns, the
-// 16-byte pieces of row r at slot ^ (r / 2) % 8, conflict-free both ways) so
-// that every global store writes whole 128-byte lines of 8 rows; the L2
-// then merges no partial lines.  Lane (r, h) writes its 8-byte groups in the
-// MFMA layout; lane L reads back 16 bytes, row L / 8 + 8 k, slot L % 8.
-__device__ __forceinline__ void fast_epilogue_full_bf16(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
-                                                        int64_t n0, int N, int wm, int wn, int r, int h, float g,
-                                                        uint8_t* wl) {
+// NJ (1 or 2) B frags j0 .. j0 + NJ - 1 of A frag i, bf16, staged through the
+// wave-private 4 KiB LDS chunk `wl` (32 rows x 128 bytes, the 16-byte pieces
+// of row r at slot ^ (r / 2) % 8, conflict-free both ways): lane (r, h) writes
+// its 8-byte groups in the MFMA layout, then lanes read back 16 bytes each so
+// that a store instruction covers 8 (NJ = 2: one whole 128-byte line per row)
+// or 16 rows (NJ = 1: 64 contiguous bytes per row).  `dst0` is the output
+// element of row 0, column 32 j0 of the run.
+template <int NJ, int FN>
+__device__ __forceinline__ void bf16_run(const f32x16 (&acc)[FN][4], int i, int j0, __bf16* __restrict__ dst0,
+                                         uint32_t N, int r, int h, float g, uint8_t* wl) {
   const int lane = threadIdx.x & 63;
   const uint32_t wsw = (uint32_t)((r >> 1) & 7);
   uint8_t* const wrow = wl + r * 128 + 8 * h;
-  const int rr0 = lane >> 3, slot = lane & 7;
-  const uint32_t out0 = (uint32_t)m0 + (uint32_t)(wm * 128);
-  const uint32_t lane_off = (uint32_t)rr0 * (uint32_t)N + (uint32_t)(n0 + wn * 128 + 8 * slot);
+#pragma unroll
+  for (int jj = 0; jj < NJ; jj++) {
+    const f32x16 a = pinned(acc[j0 + jj][i]);
+#pragma unroll
+    for (int gq = 0; gq < 4; gq++) {
+      const uint32_t chunk = (uint32_t)(4 * jj + gq);
+      *reinterpret_cast<u32x2*>(wrow + 16 * (chunk ^ wsw)) = u32x2{bf16_pair(a, gq, 0, g), bf16_pair(a, gq, 1, g)};
+    }
+  }
+  constexpr int kLanesPerRow = 4 * NJ, kRowsPerStore = 64 / kLanesPerRow;
+  const int rr0 = lane / kLanesPerRow, slot = lane % kLanesPerRow;
+#pragma unroll
+  for (int k = 0; k < 32 / kRowsPerStore; k++) {
+    const int rr = rr0 + kRowsPerStore * k;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wl + rr * 128 + 16 * (slot ^ ((rr >> 1) & 7)));
+    *reinterpret_cast<u32x4*>(dst0 + ((uint32_t)rr * N + 8u * (uint32_t)slot)) = v;
+  }
+}
+
+// Full tiles of an output with fewer than 2^32 elements, bf16, through the
+// wave's LDS chunk so that the stores write whole 128-byte lines: pairs of
+// adjacent B frags (64 columns, 128 bytes, 128-byte aligned since the tile's
+// column offset is a multiple of 64).  With FN = 3 wave 0 covers columns
+// 0-95 of the tile (frags 0-1 paired, frag 2 alone) and wave 1 columns 96-191
+// (frag 0 alone, frags 1-2 paired): the two single frags share one line.
+template <int FN>
+__device__ __forceinline__ void fast_epilogue_full_bf16(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
+                                                        int64_t n0, int N, int wm, int wn, int r, int h, float g,
+                                                        uint8_t* wl) {
+  const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128), col0 = (uint32_t)n0 + (uint32_t)(wn * 32 * FN);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-#pragma unroll
-    for (int jp = 0; jp < 2; jp++) {
-#pragma unroll
-      for (int jj = 0; jj < 2; jj++) {
-        const f32x16 a = pinned(acc[2 * jp + jj][i]);
-#pragma unroll
-        for (int gq = 0; gq < 4; gq++) {
-          const uint32_t chunk = (uint32_t)(4 * jj + gq);
-          *reinterpret_cast<u32x2*>(wrow + 16 * (chunk ^ wsw)) = u32x2{bf16_pair(a, gq, 0, g), bf16_pair(a, gq, 1, g)};
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const int rr = rr0 + 8 * k;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(wl + rr * 128 + 16 * (slot ^ ((rr >> 1) & 7)));
-        __bf16* dst = reinterpret_cast<__bf16*>(c) + ((out0 + 32u * i + 8u * k) * (uint32_t)N + lane_off + 64u * jp);
-        *reinterpret_cast<u32x4*>(dst) = v;
-      }
+    __bf16* d = reinterpret_cast<__bf16*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
+    if constexpr (FN == 4) {
+      bf16_run<2>(acc, i, 0, d, (uint32_t)N, r, h, g, wl);
+      bf16_run<2>(acc, i, 2, d + 64, (uint32_t)N, r, h, g, wl);
+    } else if (wn == 0) {
+      bf16_run<2>(acc, i, 0, d, (uint32_t)N, r, h, g, wl);
+      bf16_run<1>(acc, i, 2, d + 64, (uint32_t)N, r, h, g, wl);
+    } else {
+      bf16_run<1>(acc, i, 0, d, (uint32_t)N, r, h, g, wl);
+      bf16_run<2>(acc, i, 1, d + 32, (uint32_t)N, r, h, g, wl);
     }
   }
 }
 
 // Full tiles, fp32 output: 16-byte stores straight from the MFMA layout.
-__device__ __forceinline__ void fast_epilogue_full_f32(const f32x16 (&acc)[4][4], void* __restrict__ c, int64_t m0,
+template <int FN>
+__device__ __forceinline__ void fast_epilogue_full_f32(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
                                                        int64_t n0, int N, int wm, int wn, int r, int h, float g) {
   const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128 + r);
-  const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 128 + 4 * h);
+  const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 32 * FN + 4 * h);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     float* row = reinterpret_cast<float*>(c) + ((row0 + 32u * i) * (uint32_t)N + col0);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < FN; j++) {
       const f32x16 a = pinned(acc[j][i]);
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) fast_store4<false>(row + 32 * j + 8 * gq, 0, a, gq, g);
@@ -733,13 +830,15 @@ __device__ __forceinline__ void fast_epilogue_full_f32(const f32x16 (&acc)[4][4]
 // the next tile's first two stages are issued during the current tile's last
 // two, and the epilogue stores are not waited for, so neither the store
 // drain, the tile turnover nor the first fetch stalls the matrix cores.
-template <bool kBf16Out>
+// Tiles are 256 x 64 FN.
+template <bool kBf16Out, int FN>
 __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_sg,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, const float* __restrict__ b_sg, int M,
     int N, int K, void* __restrict__ c, int tiles_m, int tiles_n) {
-  __shared__ FastStage st0;
-  __shared__ FastStage st1;
+  constexpr int kTN = 64 * FN;  // B rows (output columns) per tile
+  __shared__ FastStage<FN> st0;
+  __shared__ FastStage<FN> st1;
   __shared__ __attribute__((aligned(16))) uint8_t epi[4][4096];  // per-wave output staging (bf16)
   const int T = tiles_m * tiles_n;
   const int G = gridDim.x;
@@ -758,20 +857,20 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   const uint32_t lds1 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)&st1);
   int tm, tn;
   tile_of_lin(lin0, tiles_m, tiles_n, tm, tn);
-  bool edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTile > N;
-  fast_load_stage(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
-                  K, 0);
-  fast_load_stage(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTile, M, N,
-                  K, 1);
+  bool edge = (int64_t)(tm + 1) * kTile > M || (int64_t)(tn + 1) * kTN > N;
+  fast_load_stage<FN>(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTN,
+                      M, N, K, 0);
+  fast_load_stage<FN>(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTN,
+                      M, N, K, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   FastLane L;
   L.a = (uint32_t)(wm * 128 + r) * 128;
-  L.b = (uint32_t)(wn * 128 + r) * 128;
+  L.b = (uint32_t)(wn * 32 * FN + r) * 128;
   L.sa = (uint32_t)(wm * 128 + r) * 16 + 2 * h;
-  L.sb = (uint32_t)(wn * 128 + r) * 16 + 2 * h;
+  L.sb = (uint32_t)(wn * 32 * FN + r) * 16 + 2 * h;
   L.hsw = 16u * (uint32_t)(h ^ ((r >> 1) & 7));
-  FastPipe P;
+  FastPipe<FN> P;
 
   for (int lin = lin0; lin < T; lin += G) {
     // First k16-step of the tile, from stage 0 in st0.  Decoding it here
@@ -781,15 +880,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     fast_read_sub(st0, P, 0, L, 0);
     fast_convert_scales(P, 0);
     fast_decode_first(P);
-    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTN;
     const bool has_next = lin + G < T;
     int tm_next = tm, tn_next = tn;
     if (has_next) tile_of_lin(lin + G, tiles_m, tiles_n, tm_next, tn_next);
-    const bool edge_next = (int64_t)(tm_next + 1) * kTile > M || (int64_t)(tn_next + 1) * kTile > N;
-    const int64_t m0_next = (int64_t)tm_next * kTile, n0_next = (int64_t)tn_next * kTile;
-    f32x16 acc[4][4];
+    const bool edge_next = (int64_t)(tm_next + 1) * kTile > M || (int64_t)(tn_next + 1) * kTN > N;
+    const int64_t m0_next = (int64_t)tm_next * kTile, n0_next = (int64_t)tn_next * kTN;
+    f32x16 acc[FN][4];
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < FN; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[j][i] = f32x16{};
     for (int kc = 0; kc < nk; kc += 2) {
@@ -799,15 +898,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
       const bool more = kc + 2 < nk;
       fast_stage(st0, st1, P, acc, L, [&] {
         if (more)
-          fast_load_stage(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
+          fast_load_stage<FN>(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
         else if (has_next)
-          fast_load_stage(lds0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 0);
+          fast_load_stage<FN>(lds0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 0);
       });
       fast_stage(st1, st0, P, acc, L, [&] {
         if (more)
-          fast_load_stage(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 3);
+          fast_load_stage<FN>(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 3);
         else if (has_next)
-          fast_load_stage(lds1, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 1);
+          fast_load_stage<FN>(lds1, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 1);
       });
     }
     // The stores drain while the next tile computes (the next wait comes
@@ -841,14 +940,27 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                    ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 16 == 0) &&
                    ((uintptr_t)b_scales % 16 == 0) && ((uintptr_t)c % 16 == 0);
   if (dma) {
-    const int T = tiles_m * tiles_n;
+    // 256 x 256 tiles, or 256 x 192 ones when those take fewer rounds of the
+    // persistent grid, a round of the smaller tiles counting as kCost192 of a
+    // full one: they hold 3/4 of the MFMA work, but the copies, barriers and
+    // epilogue per tile shrink less (measured 0.81-0.93 on 2048-8192 x 3072 x
+    // 3072).  4096 x 3072 outputs: 192 tiles of 256 x 256 leave a quarter of
+    // 256 CUs idle; 256 tiles of 256 x 192 fill them.
+    constexpr double kCost192 = 0.87;
     const int cus = device_cu_count();
+    const int64_t tn192 = (N + 191) / 192;
+    const int64_t rounds256 = ((int64_t)tiles_m * tiles_n + cus - 1) / cus;
+    const int64_t rounds192 = ((int64_t)tiles_m * tn192 + cus - 1) / cus;
+    const bool t192 = (double)rounds192 * kCost192 < (double)rounds256;
+    const int tn = t192 ? (int)tn192 : tiles_n;
+    const int T = tiles_m * tn;
     const dim3 pgrid((unsigned)(T < cus ? T : cus));
-    if (bf)
-      return launch_kernel(gemm_w4a4_fast_kernel<true>, pgrid, dim3(256), 0, stream, a_codes, a_scales, a_sg, b_codes,
-                           b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
-    return launch_kernel(gemm_w4a4_fast_kernel<false>, pgrid, dim3(256), 0, stream, a_codes, a_scales, a_sg, b_codes,
-                         b_scales, b_sg, (int)M, (int)N, (int)K, c, tiles_m, tiles_n);
+#define NVFP4_FAST_LAUNCH(B, FN)                                                                                  \
+  launch_kernel(gemm_w4a4_fast_kernel<B, FN>, pgrid, dim3(256), 0, stream, a_codes, a_scales, a_sg, b_codes, b_scales, \
+                b_sg, (int)M, (int)N, (int)K, c, tiles_m, tn)
+    if (t192) return bf ? NVFP4_FAST_LAUNCH(true, 3) : NVFP4_FAST_LAUNCH(false, 3);
+    return bf ? NVFP4_FAST_LAUNCH(true, 4) : NVFP4_FAST_LAUNCH(false, 4);
+#undef NVFP4_FAST_LAUNCH
   }
 #define NVFP4_GEMM_LAUNCH(F, B)                                                                      \
   launch_kernel(gemm_w4a4_kernel<WM, WN, F, B>, grid, block, 0, stream, a_codes, a_scales, a_sg, b_codes, \

@@ -158,3 +158,36 @@ def test_fused_act_given_scale_matches_computed():
         ref = nv.quantize(a, s_g=half)
         torch.cuda.synchronize()
         assert torch.equal(q4[0], ref[0]) and torch.equal(q4[1], ref[1]) and torch.equal(c4, nv.gemm(ref, wq))
+
+
+def _fast_tile_cols(M, N, cus=256):
+    """Output columns per tile the fast path takes (its launcher's rule on a 256-CU device):
+    256, or 192 when 256 x 192 tiles need fewer rounds of the persistent grid (a round of them
+    counting 0.87 of a 256 x 256 round)."""
+    tm = (M + 255) // 256
+    r256 = (tm * ((N + 255) // 256) + cus - 1) // cus
+    r192 = (tm * ((N + 191) // 192) + cus - 1) // cus
+    return 192 if r192 * 0.87 < r256 else 256
+
+
+@pytest.mark.parametrize("M,N,K,cols", [(512, 384, 512, 192), (520, 400, 1024, 192), (4096, 4096, 512, 256),
+                                        (4000, 4000, 512, 256), (4096, 3072, 512, 192)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_fast_tile_shapes(M, N, K, cols, out):
+    """Both output tiles of the direct-to-LDS kernel, 256 x 256 and 256 x 192, with full tiles
+    (the staged bf16 epilogue, whole and shared 128-byte lines) and ragged last tiles."""
+    assert _fast_tile_cols(M, N) == cols
+    log("gemm fast tiles", M, N, K, "tile cols", cols, out)
+    nv = _nv()
+    a = _rand((M, K), M + 3 * N)
+    b = _rand((N, K), N + 5 * M)
+    aq, bq = nv.quantize(a.to(dev())), nv.quantize(b.to(dev()))
+    c = nv.gemm(aq, bq, out_dtype=out)
+    ao, bo = oracle.quantize(oracle_input(a)), oracle.quantize(oracle_input(b))
+    if M * N <= 600 * 600:
+        ref, tot = oracle.gemm_ref(*ao, *bo)
+        check_gemm_bound(c_to_f64(c), ref, tot, out == torch.bfloat16, "fast tiles %dx%dx%d" % (M, N, K))
+    else:
+        check_gemm_tiles(c_to_f64(c), ao, bo, out == torch.bfloat16, "fast tiles %dx%dx%d" % (M, N, K), tile=128)
+    if out == torch.bfloat16:
+        assert torch.equal(nv.gemm(aq, bq, out_dtype=torch.float32).to(torch.bfloat16), c)
