@@ -365,15 +365,17 @@ __device__ __forceinline__ float sq_err8_f32(const float* xs, uint32_t w, float 
   return acc;
 }
 
-// True when the block (f0, f1) encoded under scale byte sb4 (codes w4a, w4b)
-// has a smaller squared error than under the usual sb6 (codes w6a, w6b).
-// First in fp32 on the block scaled by 2^-g_exp (exact; a block whose two
-// candidates differ lies below ~2600 s_g, so nothing overflows): each sum is
-// within 18 2^-24 of its exact value, so a difference beyond 2^-16 of their sum
-// decides, provided the sums are far from the fp32 subnormal range.  Otherwise
-// (near-ties, exact ties, sums of zero) the fp64 comparison decides.
-__device__ __forceinline__ bool prefer4(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
-                                        uint32_t sb6, uint32_t w4a, uint32_t w4b, uint32_t sb4, const EncodeConsts& c) {
+// Whether the block (f0, f1) encoded under scale byte sb4 (codes w4a, w4b)
+// has a smaller squared error than under the usual sb6 (codes w6a, w6b), in
+// fp32 on the block scaled by 2^-g_exp (exact; a block whose two candidates
+// differ lies below ~2600 s_g, so nothing overflows): each sum is within
+// 18 2^-24 of its exact value, so a difference beyond 2^-16 of their sum
+// decides, provided the sums are far from the fp32 subnormal range.  Returns
+// 1 (sb4), 0 (sb6) or -1: undecided (near-ties, exact ties, sums of zero),
+// for prefer4_f64 to settle.  No calls: it sits in the encode loops.
+__device__ __forceinline__ int prefer4_fast(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
+                                            uint32_t sb6, uint32_t w4a, uint32_t w4b, uint32_t sb4,
+                                            const EncodeConsts& c) {
   const float v6 = e4m3_value(sb6), v4 = e4m3_value(sb4);
   float xs[16];
 #pragma unroll
@@ -385,10 +387,19 @@ __device__ __forceinline__ bool prefer4(const float (&f0)[8], const float (&f1)[
   const float e4 = sq_err8_f32(xs + 8, w4b, v4, c.g_norm, sq_err8_f32(xs, w4a, v4, c.g_norm, 0.0f));
   const float sum = e6 + e4, diff = e6 - e4, tol = 0x1p-16f * sum;
   if (__builtin_expect(sum >= 0x1p-100f, 1)) {
-    if (diff > tol) return true;
-    if (diff < -tol) return false;
+    if (diff > tol) return 1;
+    if (diff < -tol) return 0;
   }
-  return prefer4_f64(f0, f1, w6a, w6b, v6, w4a, w4b, v4, c.s_g);
+  return -1;
+}
+
+// The same decision, always settled (prefer4_fast, then the fp64 and exact
+// comparisons).
+__device__ __forceinline__ bool prefer4(const float (&f0)[8], const float (&f1)[8], uint32_t w6a, uint32_t w6b,
+                                        uint32_t sb6, uint32_t w4a, uint32_t w4b, uint32_t sb4, const EncodeConsts& c) {
+  const int d = prefer4_fast(f0, f1, w6a, w6b, sb6, w4a, w4b, sb4, c);
+  if (d >= 0) return d == 1;
+  return prefer4_f64(f0, f1, w6a, w6b, e4m3_value(sb6), w4a, w4b, e4m3_value(sb4), c.s_g);
 }
 
 // RN_bf16 of the exact product p * s_g, where p = val(code) * val(scale) is

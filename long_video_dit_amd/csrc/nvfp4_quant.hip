@@ -194,10 +194,14 @@ struct Raw8<float> {
 // (always in bounds) and the stores need no predicate.
 // The scale byte and the two code words of one 16-element block: the usual
 // encoding, or with k46 (FourOverSix) the one of the two candidate scales that
-// dequantizes with the smaller squared error.
+// dequantizes with the smaller squared error.  Returns false when k46 and the
+// fast comparison cannot decide (a near-tie): the caller settles the block
+// with encode_block_settle, outside its loop (that path calls functions, and
+// a call inside the encode loops makes the compiler spill to scratch on every
+// block).
 template <bool k46>
-__device__ __forceinline__ void encode_block(const float (&f0)[8], const float (&f1)[8], float am, const EncodeConsts& c,
-                                             uint32_t& sb, uint32_t& w0, uint32_t& w1) {
+__device__ __forceinline__ bool encode_block(const float (&f0)[8], const float (&f1)[8], float am,
+                                             const EncodeConsts& c, uint32_t& sb, uint32_t& w0, uint32_t& w1) {
   sb = encode_scale(am, c);
   w0 = encode8(f0, sb, c);
   w1 = encode8(f1, sb, c);
@@ -205,19 +209,50 @@ __device__ __forceinline__ void encode_block(const float (&f0)[8], const float (
     const uint32_t sb4 = encode_scale4(am, c);
     if (sb4 != sb) {
       const uint32_t x0 = encode8(f0, sb4, c), x1 = encode8(f1, sb4, c);
-      if (prefer4(f0, f1, w0, w1, sb, x0, x1, sb4, c)) {
+      const int d = prefer4_fast(f0, f1, w0, w1, sb, x0, x1, sb4, c);
+      if (d < 0) return false;
+      if (d == 1) {
         sb = sb4;
         w0 = x0;
         w1 = x1;
       }
     }
   }
+  return true;
 }
+
+// FourOverSix encoding of one block with the decision always settled (the
+// fp64 and exact comparisons after the fast one).
+__device__ __noinline__ void encode_block_settle(const float (&f0)[8], const float (&f1)[8], float s_g,
+                                                 uint32_t& sb, uint32_t& w0, uint32_t& w1) {
+  const EncodeConsts c = make_encode_consts(s_g);  // built here: a reference would put it in scratch
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(f0[i]), __builtin_fabsf(f1[i])));
+  sb = encode_scale(am, c);
+  w0 = encode8(f0, sb, c);
+  w1 = encode8(f1, sb, c);
+  const uint32_t sb4 = encode_scale4(am, c);
+  if (sb4 != sb) {
+    const uint32_t x0 = encode8(f0, sb4, c), x1 = encode8(f1, sb4, c);
+    if (prefer4(f0, f1, w0, w1, sb, x0, x1, sb4, c)) {
+      sb = sb4;
+      w0 = x0;
+      w1 = x1;
+    }
+  }
+}
+
+// Blocks of a workgroup whose FourOverSix decision is left to after its
+// encode loop: entries (iteration << 8 | thread), at most 4 per thread (the
+// launcher sizes the grid for that).
+constexpr int kPendMax = 4 * kThreads;
 
 template <typename T, bool k46>
 __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int64_t nb, int64_t b0, int64_t stride,
                                                    const EncodeConsts& c, uint32_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales, int64_t base) {
+                                                   uint8_t* __restrict__ scales, int64_t base, uint32_t* pend,
+                                                   uint32_t* npend) {
   const int64_t last = nb - 1;
   Raw8<T> nxt[2];
   {
@@ -225,7 +260,8 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
     nxt[0].load(xg, 2 * bb);
     nxt[1].load(xg, 2 * bb + 1);
   }
-  for (int64_t bk = b0; bk < nb; bk += stride) {
+  uint32_t it = 0;
+  for (int64_t bk = b0; bk < nb; bk += stride, it++) {
     const Raw8<T> cur[2] = {nxt[0], nxt[1]};
     const int64_t bn = __builtin_elementwise_min(bk + stride, last);
     nxt[0].load(xg, 2 * bn);
@@ -238,10 +274,26 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
     for (int i = 0; i < 8; i++)
       am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(f0[i]), __builtin_fabsf(f1[i])));
     uint32_t sb, w0, w1;
-    encode_block<k46>(f0, f1, am, c, sb, w0, w1);
+    if (!encode_block<k46>(f0, f1, am, c, sb, w0, w1)) {
+      pend[atomicAdd(npend, 1u)] = (it << 8) | threadIdx.x;
+      continue;
+    }
     __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(codes + base) + bk);
     scales[(base >> 1) + bk] = (uint8_t)sb;
   }
+}
+
+// The loop with the encoder's mode read at run time (a tiny or zero s_g), as
+// a function of its own for FourOverSix: its calls need registers saved across
+// them, and inside the kernel the compiler would hoist those scratch stores
+// ahead of the usual-mode loop as well.
+template <typename T, bool k46>
+__device__ __noinline__ void encode_lane_blocks_any_mode(const T* __restrict__ xg, int64_t nb, int64_t b0,
+                                                         int64_t stride, float s_g, uint32_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, int64_t base, uint32_t* pend,
+                                                         uint32_t* npend) {
+  const EncodeConsts c = make_encode_consts(s_g);  // built here: a reference would put it in scratch
+  encode_lane_blocks<T, k46>(xg, nb, b0, stride, c, codes, scales, base, pend, npend);
 }
 
 // grid: (X, G).  Each lane encodes whole 16-element blocks.  Group g reads
@@ -252,13 +304,21 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
 // are even (whole blocks), so the 8-byte code stores stay aligned.  The
 // common case (an ordinary per-tensor scale) runs a copy of the loop in which
 // the encoder's mode is the constant 0, so that no mode test is left inside.
-// k46: FourOverSix block scaling.
+// k46: FourOverSix block scaling; the workgroup settles its undecided blocks
+// after the loop.
 template <typename T, bool k46>
-__global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ x, int64_t units_per_group,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k46 ? 4 : 1, 8))) void encode_kernel(
+    const T* __restrict__ x, int64_t units_per_group,
                                                           const float* __restrict__ s_g,
                                                           uint32_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, int64_t out_group_stride,
                                                           int64_t out_offset) {
+  __shared__ uint32_t pend[k46 ? kPendMax : 1];
+  __shared__ uint32_t npend;
+  if (k46) {
+    if (threadIdx.x == 0) npend = 0;
+    __syncthreads();
+  }
   const int g = blockIdx.y;
   const EncodeConsts c = make_encode_consts(s_g[g]);
   const int64_t base = (int64_t)g * out_group_stride + out_offset;
@@ -269,9 +329,29 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const T* __restrict__ 
   if (c.mode == 0) {
     EncodeConsts cf = c;
     cf.mode = 0;
-    encode_lane_blocks<T, k46>(xg, nb, b0, stride, cf, codes, scales, base);
+    encode_lane_blocks<T, k46>(xg, nb, b0, stride, cf, codes, scales, base, pend, &npend);
+  } else if constexpr (k46) {
+    encode_lane_blocks_any_mode<T, k46>(xg, nb, b0, stride, c.s_g, codes, scales, base, pend, &npend);
   } else {
-    encode_lane_blocks<T, k46>(xg, nb, b0, stride, c, codes, scales, base);
+    encode_lane_blocks<T, k46>(xg, nb, b0, stride, c, codes, scales, base, pend, &npend);
+  }
+  if constexpr (k46) {
+    __syncthreads();
+    const uint32_t n = npend;
+    for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+      const uint32_t ent = pend[e];
+      const int64_t bk = (int64_t)blockIdx.x * kThreads + (ent & 0xffu) + (int64_t)(ent >> 8) * stride;
+      Raw8<T> r0, r1;
+      r0.load(xg, 2 * bk);
+      r1.load(xg, 2 * bk + 1);
+      float f0[8], f1[8];
+      r0.unpack(f0);
+      r1.unpack(f1);
+      uint32_t sb, w0, w1;
+      encode_block_settle(f0, f1, c.s_g, sb, w0, w1);
+      __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(codes + base) + bk);
+      scales[(base >> 1) + bk] = (uint8_t)sb;
+    }
   }
 }
 
@@ -364,6 +444,12 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
   // Staging: codes [kTC = 128 columns][32 words + 2 pad], scales [128 columns][16 B].
   __shared__ uint32_t sc[kTC][34];
   __shared__ uint32_t ss[kTC][4];
+  __shared__ uint32_t pend[k46 ? 4 * kTThreads : 1];  // (column j << 9 | thread) of undecided FourOverSix blocks
+  __shared__ uint32_t npend;
+  if (k46) {
+    if (threadIdx.x == 0) npend = 0;
+    __syncthreads();
+  }
   const EncodeConsts c = make_encode_consts(s_g[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tiles_c = (cols + kTC - 1) / kTC;
@@ -397,12 +483,32 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
         hi[i] = f[j][8 + i];
       }
       uint32_t sb, w0, w1;
-      encode_block<k46>(lo, hi, am, c, sb, w0, w1);
+      if (!encode_block<k46>(lo, hi, am, c, sb, w0, w1)) pend[atomicAdd(&npend, 1u)] = ((uint32_t)j << 9) | threadIdx.x;
       *reinterpret_cast<u32x2*>(&sc[4 * c4 + j][2 * rb]) = u32x2{w0, w1};
       reinterpret_cast<uint8_t*>(ss[4 * c4 + j])[rb] = (uint8_t)sb;
     }
   }
   __syncthreads();
+  if constexpr (k46) {  // settle the undecided blocks in the staging buffers
+    const uint32_t n = npend;
+    for (uint32_t e = threadIdx.x; e < n; e += kTThreads) {
+      const uint32_t ent = pend[e], t = ent & 511u, j = ent >> 9;
+      const int ln = (int)(t & 63u), wv = (int)(t >> 6);
+      const int rbe = 4 * (wv & 3) + (ln >> 4), c4e = (ln & 15) + 16 * (wv >> 2);
+      const T* col = x + (tr0 + 16 * rbe) * cols + tc0 + 4 * c4e + j;
+      float lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        lo[i] = load1(col + i * cols);
+        hi[i] = load1(col + (8 + i) * cols);
+      }
+      uint32_t sb, w0, w1;
+      encode_block_settle(lo, hi, c.s_g, sb, w0, w1);
+      *reinterpret_cast<u32x2*>(&sc[4 * c4e + j][2 * rbe]) = u32x2{w0, w1};
+      reinterpret_cast<uint8_t*>(ss[4 * c4e + j])[rbe] = (uint8_t)sb;
+    }
+    __syncthreads();
+  }
   // Codes: 16 lanes per column, lane p stores rows 16 p .. 16 p + 15 (8 B).
   const int64_t words_per_col = rows / 8;
 #pragma unroll
@@ -505,7 +611,10 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
   // about three blocks per thread, up to 64 workgroups per CU: on a KV tensor
   // 6% faster than 16 per CU (and slower again at 128); on [16384, 3072] one
   // block per thread was slower than three
-  const int bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
+  int64_t bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
+  // FourOverSix: at most 4 blocks per thread, so a workgroup's undecided
+  // blocks always fit its list (kPendMax)
+  if (four_over_six) bx = std::max<int64_t>(bx, (units_per_group / 2 + kPendMax - 1) / kPendMax);
   const dim3 grid((unsigned)bx, (unsigned)groups);
   auto go = [&](auto kernel, const auto* xt) {
     return launch_kernel(kernel, grid, dim3(kThreads), 0, stream, xt, units_per_group, s_g, codes, scales,
