@@ -66,8 +66,6 @@ def parse():
     p.add_argument("--no-secondary", action="store_true", help="skip the quantize / KV-cache bandwidth lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
-    p.add_argument("--oracle-sample-rows", type=int, default=0,
-                   help=argparse.SUPPRESS)  # internal: time the oracle sample in this process (no GPU) and exit
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the step: time every workload (quantize, GEMM, KV cache) and the oracle "
                         "on a bounded sample of each, one JSON line")
@@ -127,13 +125,6 @@ def gemm_traffic(root):
 
 def main():
     args = parse()
-    if args.oracle_sample_rows:
-        root = os.path.dirname(os.path.abspath(__file__))
-        sys.path.insert(0, root)
-        import workloads
-        dt, threads = oracle_sample(workloads, args.oracle_sample_rows)
-        print(json.dumps({"seconds": dt, "threads": threads}), flush=True)
-        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the NVFP4 hot path runs on a single MI355X here; "
               "--gpus %d is not supported (multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
@@ -264,8 +255,10 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
           torch.empty(1, dtype=torch.float32, device=dev))
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     cold = {}
-    ms_c = time_cold(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2]), flush, 10)
-    ms = time_calls(torch, lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2]), 10, 2)
+    q4f = lambda: nvfp4.quantize(a4, out=q4[:2], s_g_out=q4[2])
+    settle(torch, q4f, 0.3)
+    ms_c = time_cold(torch, q4f, flush, 10)
+    ms = time_calls(torch, q4f, 30, 2)
     n = a4.numel()
     cold["quantize_ffn_down_act"] = {"shape": [M4, K4], "ms": round(ms_c, 4),
                                      "GB/s": round(n * (B_AMAX + B_ENCODE) / (ms_c * 1e-3) / 1e9, 1)}
@@ -291,7 +284,8 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
         nvfp4.kv_dequantize(*qk, out=ok)
         nvfp4.kv_dequantize(*qv, out=ov)
 
-    ms = time_calls(torch, rt, 10, 2)
+    settle(torch, rt, 0.3)
+    ms = time_calls(torch, rt, 30, 2)
     ms_c = time_cold(torch, rt, flush, 10)
     n = 2 * k.numel()
     res["kv_cache_roundtrip"] = {"shape": [H, T, D], "tensors": 2, "ms": round(ms, 4),
@@ -327,8 +321,8 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     res["kv_rope_append"] = {"heads": H, "tokens_new": Tq, "head_dim": D, "ms": round(ms_r, 4),
                              "GB/s": round(kn.numel() * (2 + 0.5625) / (ms_r * 1e-3) / 1e9, 1)}
     del qa, oa, wsa, kn
-    ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 10, 2)
-    ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 10, 2)
+    ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 30, 2)
+    ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 30, 2)
     ms_q46 = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk, four_over_six=True), 10, 2)
     res["kv_quantize"] = {"ms": round(ms_q, 4), "GB/s": round(k.numel() * (B_AMAX + B_ENCODE) / (ms_q * 1e-3) / 1e9, 1)}
     res["kv_quantize_four_over_six"] = {
@@ -594,10 +588,10 @@ def oracle_sample(workloads, rows):
 
 
 def cpu_baseline(workloads, M, N, K, rows=8192, rows_1t=128):
-    """The oracle on the host's cores (all threads, `rows` rows) and on one thread
-    (a child process with OMP_NUM_THREADS=1, `rows_1t` rows), each as TFLOP/s of
-    the same 2 M N K metric scaled by the rows it computed."""
-    import subprocess
+    """The oracle on the host's cores: all threads on `rows` rows, then one thread
+    on `rows_1t` rows, each as TFLOP/s of the same 2 M N K metric scaled by the
+    rows it computed."""
+    import oracle
 
     dt, threads = oracle_sample(workloads, rows)
     sample = ("amax of the full A [%d, %d], quantize of its first %%d rows, fp64 reference GEMM of those rows "
@@ -605,15 +599,13 @@ def cpu_baseline(workloads, M, N, K, rows=8192, rows_1t=128):
     out = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
            "kind": "oracle", "seconds": round(dt, 2), "sample": sample % rows, "cpu_model": cpu_model(),
            "host_cpus": os.cpu_count()}
-    env = dict(os.environ, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-sample-rows", str(rows_1t)],
-                       env=env, capture_output=True, text=True, timeout=600)
-    if r.returncode == 0:
-        d = json.loads(r.stdout.strip().splitlines()[-1])
-        out["single_thread"] = {"value": round(2.0 * rows_1t * N * K / d["seconds"] / 1e12, 6), "cores": d["threads"],
-                                "seconds": round(d["seconds"], 2), "sample": sample % rows_1t}
-    else:
-        log("single-thread oracle run failed:", r.stderr[-500:])
+    oracle.set_num_threads(1)
+    try:
+        dt1, t1 = oracle_sample(workloads, rows_1t)
+    finally:
+        oracle.set_num_threads(threads)
+    out["single_thread"] = {"value": round(2.0 * rows_1t * N * K / dt1 / 1e12, 6), "cores": t1,
+                            "seconds": round(dt1, 2), "sample": sample % rows_1t}
     return out
 
 

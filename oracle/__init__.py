@@ -54,6 +54,7 @@ def _load():
     sig = {
         "orc_version": (c_i, []),
         "orc_num_threads": (c_i, []),
+        "orc_set_num_threads": (None, [c_i]),
         "orc_e2m1_value": (c_d, [c_i]),
         "orc_e4m3_value": (c_d, [c_i]),
         "orc_global_scale": (c_f, [c_f]),
@@ -111,6 +112,11 @@ def _dtype_of(x):
 
 def num_threads():
     return _load().orc_num_threads()
+
+
+def set_num_threads(n):
+    """OpenMP threads of the oracle's loops from now on (results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---- scalar format functions -------------------------------------------

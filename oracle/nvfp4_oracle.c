@@ -58,6 +58,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the OpenMP loops that follow (timing on one core or on all);
+ * the results do not depend on it. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---- scalar formats -------------------------------------------------- */
 
 /* bf16 bit pattern -> its exact value. */
