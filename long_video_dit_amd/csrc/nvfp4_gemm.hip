@@ -358,6 +358,15 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, ui
 #pragma clang diagnostic pop
 
 constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code bytes per row
+// Where a stage's refill goes (see fast_stage): the waves synchronize after
+// k16-step kBarrierStep, kRefillBurst copies follow at once, and the rest come
+// one after every kRefillEvery-th MFMA block from step kRefillStep on.  On the
+// FFN shapes this is ~2% faster than issuing all copies at the barrier; the
+// matrix cores lose less time to the CU's address unit.
+constexpr int kBarrierStep = 11;
+constexpr int kRefillStep = 12;
+constexpr int kRefillBurst = 10;
+constexpr int kRefillEvery = 2;
 
 // The fast path's output tile is 256 rows of A by 64 FN rows of B: each of
 // the 4 waves (2 x 2) holds 128 rows x 32 FN columns, FN = 4 (256 x 256) or
@@ -457,6 +466,78 @@ __device__ __forceinline__ void fast_load_stage(uint32_t lds, const FastLoad& o,
     lds_dma16(b_scales + kc * 16, (uint32_t)(rb * srow_bytes), lds + S::kSB + d0);
   }
 }
+
+// The copies of one stage issued one at a time, so that part of a refill can
+// be spread between MFMA blocks: issued in one burst, the 4 waves' 18 copies
+// keep the CU's address unit busy ~1300 cycles, during which the matrix cores
+// wait.  copy<k>() issues this wave's copy k of fast_load_stage's full-tile
+// path (k < 8: A codes, then 2 FN B codes, then A's and B's scale rows) from
+// sources and LDS destinations set up once per stage; burst<n>() copies
+// 0 .. n - 1.  A tile that crosses row M or column N has its stage issued
+// whole (whole_stage()) instead.
+template <int FN>
+struct FastRefill {
+  static constexpr int kCopies = 8 + 2 * FN + 2;
+  const uint8_t *ac, *bc, *as, *bs;  // this wave's sources of copy 0 of each kind
+  int64_t row8;                      // 8 rows of codes in bytes
+  uint32_t la, lb, lsa, lsb;         // this wave's LDS destinations of copy 0 of each kind
+  FastLoad o;
+  bool split, split_sb;              // full tile: copies one at a time (B scales: only the first FN waves)
+  bool whole;                        // edge tile: the stage in one go, with the arguments below
+  const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+  int64_t m0, n0;
+  int M, N, K, kc;
+  uint32_t lds;
+
+  __device__ __forceinline__ FastRefill(uint32_t lds_, const FastLoad& o_, bool on, bool edge,
+                                        const uint8_t* __restrict__ a_codes_, const uint8_t* __restrict__ a_scales_,
+                                        const uint8_t* __restrict__ b_codes_, const uint8_t* __restrict__ b_scales_,
+                                        int64_t m0_, int64_t n0_, int M_, int N_, int K_, int kc_)
+      : o(o_), a_codes(a_codes_), a_scales(a_scales_), b_codes(b_codes_), b_scales(b_scales_), m0(m0_), n0(n0_),
+        M(M_), N(N_), K(K_), kc(kc_), lds(lds_) {
+    using S = FastStage<FN>;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row_bytes = K / 2, srow_bytes = K / 16;
+    split = on && !edge;
+    split_sb = split && (FN == 4 || w < FN);
+    whole = on && edge;
+    row8 = 8 * row_bytes;
+    ac = a_codes + (m0 + 64 * w) * row_bytes + kc * 128;
+    bc = b_codes + (n0 + 16 * FN * w) * row_bytes + kc * 128;
+    as = a_scales + (m0 + 64 * w) * srow_bytes + kc * 16;
+    bs = b_scales + (n0 + 64 * w) * srow_bytes + kc * 16;
+    la = lds + S::kA + (uint32_t)(w * 8) * 64 * 16;
+    lb = lds + S::kB + (uint32_t)(w * 2 * FN) * 64 * 16;
+    lsa = lds + S::kSA + (uint32_t)w * 64 * 16;
+    lsb = lds + S::kSB + (uint32_t)w * 64 * 16;
+  }
+
+  __device__ __forceinline__ void whole_stage() const {
+    if (whole) fast_load_stage<FN>(lds, o, true, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc);
+  }
+
+  template <int n, int k = 0>
+  __device__ __forceinline__ void burst() const {
+    if constexpr (k < n) {
+      copy<k>();
+      burst<n, k + 1>();
+    }
+  }
+
+  template <int k>
+  __device__ __forceinline__ void copy() const {
+    if constexpr (k < 8) {
+      if (split) lds_dma16(ac + k * row8, o.vo[k & 1], la + (uint32_t)k * 64 * 16);
+    } else if constexpr (k < 8 + 2 * FN) {
+      constexpr int i = k - 8;
+      if (split) lds_dma16(bc + i * row8, o.vo[i & 1], lb + (uint32_t)i * 64 * 16);
+    } else if constexpr (k == 8 + 2 * FN) {
+      if (split) lds_dma16(as, o.vs, lsa);
+    } else if constexpr (k == 9 + 2 * FN) {
+      if (split_sb) lds_dma16(bs, o.vs, lsb);
+    }
+  }
+};
 
 // Registers that carry the pipeline from step to step: the packed codes and
 // fp16 scale pairs of two sub-chunks (sub-chunk s of a stage uses buffer
@@ -633,7 +714,10 @@ __device__ __forceinline__ void mfma4_decode3(f32x16& c0, f32x16& c1, f32x16& c2
 // frags; with FN = 3 block 2 decodes all three B frags.
 template <int n, int FN>
 __device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& P, f32x16 (&acc)[FN][4],
-                                          const FastLane& L) {
+                                          const FastLane& L, const FastRefill<FN>& rf) {
+  // copies of the refill after every kRefillEvery-th MFMA block from step kRefillStep on (3 or 4 blocks a step)
+  constexpr int kBlocks = FN == 4 ? 4 : 3;
+  constexpr int j0 = (n - kRefillStep) * kBlocks;  // MFMA block index from the first refill step
   constexpr int s = n >> 2, t = n & 3;
   if constexpr (t == 0 && s < 3) fast_read_sub(S, P, (s + 1) & 1, L, s + 1);
   if constexpr (t == 2 && s < 3) fast_convert_scales(P, (s + 1) & 1);
@@ -646,50 +730,60 @@ __device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& 
   const uint4* B = P.cb[u1];
   mfma4_decode2<hi>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
                     word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1]);
+  if constexpr (n >= kRefillStep && (j0 + 0) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 0) / kRefillEvery>();
   mfma4_decode2<hi>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
                     word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3]);
+  if constexpr (n >= kRefillStep && (j0 + 1) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 1) / kRefillEvery>();
   if constexpr (FN == 4) {
     mfma4_decode2<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
                       word_of(B[1], t1), P.sb[u1][1], P.bv[x][0], P.bv[x][1]);
+    if constexpr (n >= kRefillStep && (j0 + 2) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 2) / kRefillEvery>();
     mfma4_decode2<hi>(acc[3][0], acc[3][1], acc[3][2], acc[3][3], P.bv[c][3], P.av[c], word_of(B[2], t1), P.sb[u1][2],
                       word_of(B[3], t1), P.sb[u1][3], P.bv[x][2], P.bv[x][3]);
+    if constexpr (n >= kRefillStep && (j0 + 3) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 3) / kRefillEvery>();
   } else {
     static_assert(FN == 3, "FN is 3 or 4");
     mfma4_decode3<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
                       word_of(B[1], t1), P.sb[u1][1], word_of(B[2], t1), P.sb[u1][2], P.bv[x][0], P.bv[x][1],
                       P.bv[x][2]);
+    if constexpr (n >= kRefillStep && (j0 + 2) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 2) / kRefillEvery>();
+  }
+}
+
+static_assert(kBarrierStep >= 8 && kBarrierStep <= 11, "S is last read at step 8; Sn is first read at step 12");
+static_assert(kRefillStep > kBarrierStep, "copies into S only after the barrier");
+
+template <int n, int FN>
+__device__ __forceinline__ void fast_stage_steps(const FastStage<FN>& S, const FastStage<FN>& Sn, FastPipe<FN>& P,
+                                                 f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf) {
+  if constexpr (n < 16) {
+    if constexpr (n == 12) fast_read_sub(Sn, P, 0, L, 0);
+    fast_step<n>(S, P, acc, L, rf);
+    if constexpr (n == kBarrierStep) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      rf.whole_stage();
+      rf.template burst<kRefillBurst>();
+    }
+    fast_stage_steps<n + 1>(S, Sn, P, acc, L, rf);
   }
 }
 
 // One stage (K = 256 = 4 sub-chunks x 4 k16-steps) from LDS stage S.  S is
-// last read at step 8, so before step 12 the waves synchronize (after which
-// every copy into Sn has landed and nobody reads S any more), `refill`
-// issues the copies of the stage after next into S, and sub-chunk 0 of Sn is
-// read for the decode carried by step 15 (after the last stage of a
-// workgroup Sn holds stale data, read but never used).
-template <int FN, typename Refill>
+// last read at step 8 (sub-chunk 3); after step kBarrierStep the waves
+// synchronize (after which every copy into Sn has landed and nobody reads S
+// any more), the copies of the stage after next into S (`rf`) are issued,
+// part at once and the rest between the MFMA blocks of the following steps,
+// and sub-chunk 0 of Sn is read at step 12 for the decode carried by step 15
+// (after the last stage of a workgroup Sn holds stale data, read but never
+// used).
+template <int FN>
 __device__ __forceinline__ void fast_stage(const FastStage<FN>& S, const FastStage<FN>& Sn, FastPipe<FN>& P,
-                                           f32x16 (&acc)[FN][4], const FastLane& L, Refill&& refill) {
-  fast_step<0>(S, P, acc, L);
-  fast_step<1>(S, P, acc, L);
-  fast_step<2>(S, P, acc, L);
-  fast_step<3>(S, P, acc, L);
-  fast_step<4>(S, P, acc, L);
-  fast_step<5>(S, P, acc, L);
-  fast_step<6>(S, P, acc, L);
-  fast_step<7>(S, P, acc, L);
-  fast_step<8>(S, P, acc, L);
-  fast_step<9>(S, P, acc, L);
-  fast_step<10>(S, P, acc, L);
-  fast_step<11>(S, P, acc, L);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  refill();
-  fast_read_sub(Sn, P, 0, L, 0);
-  fast_step<12>(S, P, acc, L);
-  fast_step<13>(S, P, acc, L);
-  fast_step<14>(S, P, acc, L);
-  fast_step<15>(S, P, acc, L);
+                                           f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf) {
+  constexpr int kBlocks = FN == 4 ? 4 : 3;
+  static_assert(kRefillBurst + (16 - kRefillStep) * kBlocks / kRefillEvery >= FastRefill<FN>::kCopies,
+                "every copy of the refill is issued within the stage");
+  fast_stage_steps<0>(S, Sn, P, acc, L, rf);
 }
 
 // Epilogue of one tile: lane (r, h), accumulator element e of MFMA tile (j, i)
@@ -896,18 +990,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
       // the stage two later: kc + 2 of this tile or, at the end of the tile,
       // stage 0 / 1 of the next tile.
       const bool more = kc + 2 < nk;
-      fast_stage(st0, st1, P, acc, L, [&] {
-        if (more)
-          fast_load_stage<FN>(lds0, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 2);
-        else if (has_next)
-          fast_load_stage<FN>(lds0, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 0);
-      });
-      fast_stage(st1, st0, P, acc, L, [&] {
-        if (more)
-          fast_load_stage<FN>(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, m0, n0, M, N, K, kc + 3);
-        else if (has_next)
-          fast_load_stage<FN>(lds1, ld, edge_next, a_codes, a_scales, b_codes, b_scales, m0_next, n0_next, M, N, K, 1);
-      });
+      // the stage two later: kc + 2 / kc + 3 of this tile, or stage 0 / 1 of the next
+      const int64_t rm0 = more ? m0 : m0_next, rn0 = more ? n0 : n0_next;
+      const bool redge = more ? edge : edge_next, ron = more || has_next;
+      const int rkc = more ? kc + 2 : 0;
+      fast_stage(st0, st1, P, acc, L,
+                 FastRefill<FN>(lds0, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K, rkc));
+      fast_stage(st1, st0, P, acc, L,
+                 FastRefill<FN>(lds1, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K, rkc + 1));
     }
     // The stores drain while the next tile computes (the next wait comes
     // 12 k16-steps later).
