@@ -122,12 +122,17 @@ __device__ __forceinline__ EncodeConsts make_encode_consts(float s_g) {
   c.g_exp = e - 1;
   c.g_norm = __builtin_ldexpf(s_g, -c.g_exp);
   c.mode = (s_g < kTinyScale) ? 2 : 0;
-  const double i6 = 1.0 / (6.0 * (double)s_g), i4 = 1.0 / (4.0 * (double)s_g);
-  c.i6_lo = (float)(i6 * (double)kBracketLo);
-  c.i6_hi = (float)(i6 * (double)kBracketHi);
-  c.i4_lo = (float)(i4 * (double)kBracketLo);
-  c.i4_hi = (float)(i4 * (double)kBracketHi);
-  c.inv_g = (float)(1.0 / (double)s_g);
+  // fp32 reciprocals (v_rcp_f32, within 1 ulp; 6 s_g and 4 s_g round by at
+  // most half an ulp, the bracket products by another): each bracket end is
+  // off by under 2^-21 relative, far inside its 2^-18 margin, so lo stays
+  // below and hi above the exact reciprocal.  In the tiny-scale mode these
+  // are unused (they may overflow there).
+  const float i6 = __builtin_amdgcn_rcpf(6.0f * s_g), i4 = __builtin_amdgcn_rcpf(4.0f * s_g);
+  c.i6_lo = i6 * kBracketLo;
+  c.i6_hi = i6 * kBracketHi;
+  c.i4_lo = i4 * kBracketLo;
+  c.i4_hi = i4 * kBracketHi;
+  c.inv_g = __builtin_amdgcn_rcpf(s_g);
   return c;
 }
 

@@ -71,15 +71,16 @@ __device__ __forceinline__ uint32_t amax8_bits(const float* __restrict__ x, int6
   return m;
 }
 
+template <int kNT = kThreads>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* smem) {
-  // wavefront reduction, then across the 4 waves of the block
+  // wavefront reduction, then across the kNT / 64 waves of the block
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = __builtin_elementwise_max(v, (uint32_t)__shfl_xor((int)v, off));
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) smem[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 1; i < kThreads / 64; i++) v = __builtin_elementwise_max(v, smem[i]);
+    for (int i = 1; i < kNT / 64; i++) v = __builtin_elementwise_max(v, smem[i]);
   }
   return v;
 }
@@ -106,14 +107,28 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const T* __restr
   if (threadIdx.x == 0) partials[(int64_t)g * gridDim.x + blockIdx.x] = m;
 }
 
-// grid: G blocks.  s_g[g] = RN_f32(max(partials of g) / 2688).
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t* __restrict__ partials, int P,
-                                                            float* __restrict__ s_g) {
-  __shared__ uint32_t smem[kThreads / 64];
+// grid: G blocks of kFinThreads.  s_g[g] = RN_f32(max(partials of g) / 2688).
+// A thread issues its (up to 4) loads of a pass before reducing them, so up
+// to 4096 partials cost one memory round trip rather than one per partial.
+constexpr int kFinThreads = 1024;
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(const uint32_t* __restrict__ partials, int P,
+                                                               float* __restrict__ s_g) {
+  __shared__ uint32_t smem[kFinThreads / 64];
   const int g = blockIdx.x;
+  const uint32_t* pg = partials + (int64_t)g * P;
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < P; i += kThreads) m = __builtin_elementwise_max(m, partials[(int64_t)g * P + i]);
-  m = block_max_u32(m, smem);
+  for (int i0 = 0; i0 < P; i0 += 4 * kFinThreads) {
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int i = i0 + j * kFinThreads + (int)threadIdx.x;
+      v[j] = i < P ? pg[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) m = __builtin_elementwise_max(m, v[j]);
+  }
+  m = block_max_u32<kFinThreads>(m, smem);
   if (threadIdx.x == 0) {
     // IEEE division is correctly rounded: one RNE of amax / 2688.
     s_g[g] = __fdiv_rn(__uint_as_float(m), 2688.0f);
@@ -152,7 +167,9 @@ __global__ void finalize_slot_kernel(float* __restrict__ s_g) {
 
 // One 8-element unit as loaded (16 B of bf16 or 32 B of fp32), converted to
 // fp32 only when it is encoded, so that the next units' loads can be issued
-// first.
+// first.  Non-temporal loads: plain ones were ~4% faster with the tensor
+// already in the caches, but ~25% slower after other data had filled the MALL
+// (its dirty lines are then written back during the read).
 template <typename T>
 struct Raw8;
 
@@ -283,6 +300,75 @@ __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int
   }
 }
 
+// Blocks per lane per pass of encode_lane_chunks: 64 bytes of bf16 or 64 of
+// fp32 per block, so 4 bf16 or 2 fp32 blocks take 32 VGPRs of loads.
+template <typename T>
+struct EncodeChunk {
+  static constexpr int kBlocks = sizeof(T) == 2 ? 4 : 2;
+};
+
+// The plain (not FourOverSix) encode of whole 16-element blocks, in passes:
+// pass p of workgroup w takes chunk ch = w + p * gridDim.x, whose lane t
+// encodes blocks ch * kBlocks * kThreads + j * kThreads + t (j < kBlocks).  A
+// pass issues all of its loads, waits for them once, then encodes and stores
+// every block.  gfx950 counts loads and stores on one counter, and the
+// compiler cannot wait for a load issued after a store without waiting for
+// the store too: a loop that loads the next block while storing the current
+// one waits each iteration for its stores to land.  Here a pass waits once,
+// for its loads and the previous pass's stores together.  Loads past the last
+// block are clamped to it (in bounds) and their stores skipped.
+template <typename T>
+struct EncodeChunkRegs {
+  Raw8<T> r[EncodeChunk<T>::kBlocks][2];
+
+  __device__ __forceinline__ void load(const T* __restrict__ xg, int64_t ch, int64_t last) {
+#pragma unroll
+    for (int j = 0; j < EncodeChunk<T>::kBlocks; j++) {
+      const int64_t bk =
+          __builtin_elementwise_min(ch * EncodeChunk<T>::kBlocks * kThreads + j * kThreads + threadIdx.x, last);
+      r[j][0].load(xg, 2 * bk);
+      r[j][1].load(xg, 2 * bk + 1);
+    }
+  }
+
+  __device__ __forceinline__ void encode(int64_t ch, int64_t nb, const EncodeConsts& c, uint32_t* __restrict__ codes,
+                                         uint8_t* __restrict__ scales, int64_t base) const {
+#pragma unroll
+    for (int j = 0; j < EncodeChunk<T>::kBlocks; j++) {
+      const int64_t bk = ch * EncodeChunk<T>::kBlocks * kThreads + j * kThreads + threadIdx.x;
+      float f0[8], f1[8];
+      r[j][0].unpack(f0);
+      r[j][1].unpack(f1);
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(f0[i]), __builtin_fabsf(f1[i])));
+      uint32_t sb, w0, w1;
+      encode_block<false>(f0, f1, am, c, sb, w0, w1);
+      if (bk < nb) {
+        __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(codes + base) + bk);
+        scales[(base >> 1) + bk] = (uint8_t)sb;
+      }
+    }
+  }
+};
+
+// The passes from the workgroup's second on; the first chunk is already in
+// flight in `rg`.
+template <typename T>
+__device__ __forceinline__ void encode_lane_chunks(EncodeChunkRegs<T>& rg, const T* __restrict__ xg, int64_t nb,
+                                                   const EncodeConsts& c, uint32_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, int64_t base) {
+  constexpr int64_t kSpan = (int64_t)EncodeChunk<T>::kBlocks * kThreads;
+  for (int64_t ch = blockIdx.x;;) {
+    __builtin_amdgcn_s_waitcnt(0);
+    rg.encode(ch, nb, c, codes, scales, base);
+    ch += gridDim.x;
+    if (ch * kSpan >= nb) break;
+    rg.load(xg, ch, nb - 1);
+  }
+}
+
 // The loop with the encoder's mode read at run time (a tiny or zero s_g), as
 // a function of its own for FourOverSix: its calls need registers saved across
 // them, and inside the kernel the compiler would hoist those scratch stores
@@ -320,20 +406,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k46 ? 
     __syncthreads();
   }
   const int g = blockIdx.y;
-  const EncodeConsts c = make_encode_consts(s_g[g]);
   const int64_t base = (int64_t)g * out_group_stride + out_offset;
   const T* xg = x + (int64_t)g * units_per_group * 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int64_t b0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t nb = units_per_group / 2;
-  if (c.mode == 0) {
+  // The plain encode issues its first chunk's loads before it reads s_g and
+  // builds the constants (two dependent scalar loads and fp64 divisions).
+  // The grid never exceeds the chunk count, so every workgroup has one.
+  EncodeChunkRegs<T> rg;
+  if constexpr (!k46) rg.load(xg, blockIdx.x, nb - 1);
+  const EncodeConsts c = make_encode_consts(s_g[g]);
+  if constexpr (!k46) {
+    if (c.mode == 0) {
+      EncodeConsts cf = c;
+      cf.mode = 0;
+      encode_lane_chunks<T>(rg, xg, nb, cf, codes, scales, base);
+    } else {
+      encode_lane_chunks<T>(rg, xg, nb, c, codes, scales, base);
+    }
+  } else if (c.mode == 0) {
     EncodeConsts cf = c;
     cf.mode = 0;
     encode_lane_blocks<T, k46>(xg, nb, b0, stride, cf, codes, scales, base, pend, &npend);
-  } else if constexpr (k46) {
-    encode_lane_blocks_any_mode<T, k46>(xg, nb, b0, stride, c.s_g, codes, scales, base, pend, &npend);
   } else {
-    encode_lane_blocks<T, k46>(xg, nb, b0, stride, c, codes, scales, base, pend, &npend);
+    encode_lane_blocks_any_mode<T, k46>(xg, nb, b0, stride, c.s_g, codes, scales, base, pend, &npend);
   }
   if constexpr (k46) {
     __syncthreads();
@@ -577,12 +674,12 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t units_per_group
     if (e != hipSuccess) return e;
   }
   // group g's partials are slices g * sub .. g * sub + sub - 1: P * sub in a row
-  return launch_kernel(finalize_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, (const uint32_t*)partials,
+  return launch_kernel(finalize_kernel, dim3((unsigned)groups), dim3(kFinThreads), 0, stream, (const uint32_t*)partials,
                        (int)(P * sub), s_g);
 }
 
 hipError_t launch_finalize(const uint32_t* partials, int P, float* s_g, hipStream_t stream) {
-  return launch_kernel(finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partials, P, s_g);
+  return launch_kernel(finalize_kernel, dim3(1), dim3(kFinThreads), 0, stream, partials, P, s_g);
 }
 
 hipError_t launch_global_scale_slot(const void* x, int dtype, int64_t units, float* s_g, hipStream_t stream) {
@@ -608,13 +705,18 @@ hipError_t launch_encode(const void* x, int dtype, int64_t units_per_group, int 
   // whole blocks: the kernel stores 8 bytes of codes per block
   if ((units_per_group | out_group_stride | out_offset) & 1) return hipErrorInvalidValue;
   const int cus = device_cu_count();
-  // about three blocks per thread, up to 64 workgroups per CU: on a KV tensor
-  // 6% faster than 16 per CU (and slower again at 128); on [16384, 3072] one
-  // block per thread was slower than three
-  int64_t bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
-  // FourOverSix: at most 4 blocks per thread, so a workgroup's undecided
-  // blocks always fit its list (kPendMax)
-  if (four_over_six) bx = std::max<int64_t>(bx, (units_per_group / 2 + kPendMax - 1) / kPendMax);
+  int64_t bx;
+  if (four_over_six) {
+    // about three blocks per thread, up to 64 workgroups per CU, and at most
+    // 4 blocks per thread, so a workgroup's undecided blocks always fit its
+    // list (kPendMax)
+    bx = grid_blocks(units_per_group, 6, std::max(1, cus * 64 / groups));
+    bx = std::max<int64_t>(bx, (units_per_group / 2 + kPendMax - 1) / kPendMax);
+  } else {
+    // one chunk of EncodeChunk blocks per thread, up to 64 workgroups per CU
+    const int kb = dtype == kDtypeF32 ? EncodeChunk<float>::kBlocks : EncodeChunk<uint16_t>::kBlocks;
+    bx = grid_blocks(units_per_group, 2 * kb, std::max(1, cus * 64 / groups));
+  }
   const dim3 grid((unsigned)bx, (unsigned)groups);
   auto go = [&](auto kernel, const auto* xt) {
     return launch_kernel(kernel, grid, dim3(kThreads), 0, stream, xt, units_per_group, s_g, codes, scales,
