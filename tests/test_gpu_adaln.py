@@ -70,8 +70,11 @@ def _run(x_cpu, shift, scale, rpg, eps, label, check_scale=True):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+# group sizes: one row, a few rows, partial last groups, several workgroups per group, groups
+# far longer than the tensor
 @pytest.mark.parametrize("rows,k,rpg", [(1, 16, 1), (4, 64, 3), (7, 272, 7), (33, 3072, 8), (9, 4096, 2),
-                                        (130, 528, 64)])
+                                        (130, 528, 64), (37, 528, 16), (200, 3072, 50), (1000, 1024, 333),
+                                        (20, 64, 1000), (517, 4096, 129)])
 def test_adaln_quantize_random(dtype, rows, k, rpg):
     log("adaln_quantize", dtype, rows, k, rpg)
     gen = torch.Generator().manual_seed(rows * 131 + k)
