@@ -5,13 +5,17 @@
 // with its own fp32 scale.  Inside a group the work unit of one lane is 8
 // consecutive elements (16 B of bf16, 32 B of fp32); in the amax pass lanes
 // 2j and 2j+1 share one 16-element block, and an encode lane owns two units,
-// a whole block.  All kernels are HBM-bound grid-stride loops.
+// a whole block.  All kernels are HBM-bound grid-stride loops; the encode
+// and dequantize passes go in chunks (a lane's loads of a pass issued
+// together and waited for once, then its stores), because loads and stores
+// share one wait counter.
 //
 //   amax_partial_kernel  pass 1: per-block max |x| -> partials (fp32 bits)
 //   finalize_kernel      per group: max of partials -> s_g = RN(amax / 2688)
 //   amax_slot_kernel     standalone s_g: atomic max into the s_g slot itself
-//   encode_kernel        pass 2: scale byte per 16, 8 codes per lane (optionally
-//                        FourOverSix: the better of two candidate scales per block)
+//   encode_kernel        pass 2: scale byte and 16 codes per block, a block
+//                        per lane (optionally FourOverSix: the better of two
+//                        candidate scales per block)
 //   encode_t_kernel      pass 2 along the other axis: NVFP4 of x^T
 //   dequant_kernel       codes + scales -> bf16 / fp32, 8 outputs per lane
 //
@@ -203,12 +207,6 @@ struct Raw8<float> {
   }
 };
 
-// The grid-stride loop of one lane over whole 16-element blocks b0,
-// b0 + stride, ... < nb of one group (units 2b and 2b + 1), so that the block
-// maximum needs no lane exchange and a lane stores 8 B of codes and its
-// block's scale byte.  The loads of the next block are issued before the
-// current one is encoded; their indexes are clamped to the last block
-// (always in bounds) and the stores need no predicate.
 // The scale byte and the two code words of one 16-element block: the usual
 // encoding, or with k46 (FourOverSix) the one of the two candidate scales that
 // dequantizes with the smaller squared error.  Returns false when k46 and the
@@ -265,6 +263,14 @@ __device__ __noinline__ void encode_block_settle(const float (&f0)[8], const flo
 // launcher sizes the grid for that).
 constexpr int kPendMax = 4 * kThreads;
 
+// The grid-stride loop of one lane over whole 16-element blocks b0,
+// b0 + stride, ... < nb of one group (units 2b and 2b + 1), used by the
+// FourOverSix mode (its arithmetic, not memory, bounds it; the chunked loop
+// below was no faster there).  The block maximum needs no lane exchange and a
+// lane stores 8 B of codes and its block's scale byte.  The loads of the next
+// block are issued before the current one is encoded; their indexes are
+// clamped to the last block (always in bounds) and the stores need no
+// predicate.
 template <typename T, bool k46>
 __device__ __forceinline__ void encode_lane_blocks(const T* __restrict__ xg, int64_t nb, int64_t b0, int64_t stride,
                                                    const EncodeConsts& c, uint32_t* __restrict__ codes,
