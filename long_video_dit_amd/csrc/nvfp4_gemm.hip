@@ -956,7 +956,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
                       M, N, K, 0);
   fast_load_stage<FN>(lds1, ld, edge, a_codes, a_scales, b_codes, b_scales, (int64_t)tm * kTile, (int64_t)tn * kTN,
                       M, N, K, 1);
-  __builtin_amdgcn_s_waitcnt(0);
+  // Wait for stage 0 only: stage 1 is first read at step 12 of stage 0, after
+  // that stage's barrier, which waits for every copy.  Loads complete in
+  // order, and stage 1's copies are this wave's last 8 + 2 FN + 1 (or one
+  // more), so at most that many outstanding means stage 0 has landed.
+  // s_waitcnt fields (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+  // lgkmcnt 11:8 left at their maxima.
+  constexpr int kStage1Copies = 8 + 2 * FN + 1;
+  __builtin_amdgcn_s_waitcnt((kStage1Copies & 15) | ((kStage1Copies >> 4) << 14) | (7 << 4) | (15 << 8));
   __syncthreads();
   FastLane L;
   L.a = (uint32_t)(wm * 128 + r) * 128;
