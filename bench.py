@@ -558,15 +558,25 @@ def settle(torch, fn, seconds=SETTLE_S):
 
 
 def cpu_model():
-    """The host CPU's model string (from /proc/cpuinfo)."""
+    """The host CPU's model string, family and model numbers (from /proc/cpuinfo;
+    virtual machines may shorten the model string)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break  # first processor only
+                    continue
+                key, val = (t.strip() for t in line.split(":", 1))
+                if key in ("model name", "cpu family", "model") and key not in fields:
+                    fields[key] = val
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    if "cpu family" in fields and "model" in fields:
+        name += " (family %s, model %s)" % (fields["cpu family"], fields["model"])
+    return name
 
 
 def oracle_sample(workloads, rows):
