@@ -136,6 +136,20 @@ def test_quantize_config_tensors_full_size(cfg):
     assert np.array_equal(y, oracle.dequantize(o[0], o[1], o[2], "bf16"))
 
 
+def test_quantize_fp32_multi_pass():
+    """An fp32 tensor of more blocks than one pass of the encode grid covers (64
+    workgroups per CU, one fp32 block per lane: 67.1M elements on 256 CUs), with a
+    ragged last chunk: bit-exact codes and scales, and the fp32 dequantization."""
+    rows, k = 8192, 8208  # 67,239,936 elements
+    log("quantize fp32 multi-pass", rows, k)
+    gen = torch.Generator().manual_seed(8208)
+    x = torch.randn(rows, k, generator=gen)
+    g, o = _quant_both(x, "fp32 %dx%d" % (rows, k))
+    y = _nv().dequantize(g[0], g[1], g[2], dtype=torch.float32).cpu().numpy()
+    want = oracle.dequantize(o[0], o[1], o[2], "f32")
+    assert np.array_equal(y.view(np.uint32), np.asarray(want).view(np.uint32))
+
+
 @pytest.mark.parametrize("rows,k,where", [(2048, 8192, "last"), (2048, 8192, "slice3"), (4096, 8192, "first"),
                                            (4096, 8192, "slice15")])
 def test_quantize_sliced_amax_outlier(rows, k, where):
