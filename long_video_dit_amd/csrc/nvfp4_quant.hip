@@ -581,18 +581,20 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
   }
   const EncodeConsts c = make_encode_consts(s_g[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Tile order: workgroup ids go round-robin over the 8 XCDs.  When the
-  // column tiles come in eights, XCD x takes the column tiles = x (mod 8) and
-  // walks down the rows, so that the eight XCDs read adjacent column tiles of
-  // the same rows, and the 8 row tiles that write one 128-byte line of a
-  // column's scale bytes (16 bytes each) run on one XCD, whose L2 merges them
-  // (3% faster than the plain row-major order on [16384, 14336]).
+  // Tile order: workgroup ids go round-robin over the 8 XCDs.  When row and
+  // column tiles both come in eights, XCD x takes the column tiles = x (mod 8)
+  // of one group of 8 row tiles at a time: the 8 row tiles that write one
+  // 128-byte line of a column's scale bytes (16 bytes each) then run together
+  // on one XCD, whose L2 merges them, and the tiles in flight cover 8 row
+  // tiles by all columns.  On dY [16384, 14336] (same process): 216 us against
+  // 222 us for row-major order, and 226 us when each XCD walked all the row
+  // tiles of a column tile (accesses spread over every row at once).
   const int64_t tiles_c = (cols + kTC - 1) / kTC, tiles_r = (rows + kTR - 1) / kTR;
   int64_t tile_r, tile_c;
-  if (tiles_c % 8 == 0) {
-    const int64_t s8 = blockIdx.x / 8;
-    tile_r = s8 % tiles_r;
-    tile_c = 8 * (s8 / tiles_r) + blockIdx.x % 8;
+  if (tiles_c % 8 == 0 && tiles_r % 8 == 0) {
+    const int64_t s8 = blockIdx.x / 8, rem = s8 % tiles_c;
+    tile_r = 8 * (s8 / tiles_c) + rem % 8;
+    tile_c = 8 * (rem / 8) + blockIdx.x % 8;
   } else {
     tile_r = blockIdx.x / tiles_c;
     tile_c = blockIdx.x % tiles_c;

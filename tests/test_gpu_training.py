@@ -34,10 +34,12 @@ def _both(x_cpu, label, s_g=None):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("rows,cols", [(16, 1), (16, 3), (48, 5), (256, 64), (272, 65), (512, 130), (4096, 3),
-                                       (784, 516), (48, 8), (272, 264), (528, 2048), (784, 2056), (528, 1024)])
+                                       (784, 516), (48, 8), (272, 264), (528, 2048), (784, 2056), (2048, 1024),
+                                       (2032, 1020)])
 def test_transposed_random(dtype, rows, cols):
-    """Tile edges in both directions, cols % 4 != 0 (scalar loads), one-block columns, and
-    column tiles in eights (the XCD tile order: 528 x 1024 and 528 x 2048) and not."""
+    """Tile edges in both directions, cols % 4 != 0 (scalar loads), one-block columns, and row
+    and column tiles both in eights (the XCD tile order: 2048 x 1024, and 2032 x 1020 with
+    ragged last tiles) or not."""
     log("quantize_transposed", dtype, rows, cols)
     gen = torch.Generator().manual_seed(rows * 31 + cols)
     x = torch.randn(rows, cols, generator=gen) * torch.exp(torch.randn(rows, 1, generator=gen))
