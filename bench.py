@@ -106,6 +106,39 @@ def time_calls(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def flop_of(M, N, K):
+    return 2.0 * M * N * K
+
+
+def time_graph(torch, fn, calls=20, replays=5):
+    """Average ms of fn() with `calls` calls captured in one HIP graph and the
+    graph replayed `replays` times (HIP events around the replays): the GPU
+    time of a call without the binding's per-call host time, which exceeds
+    the kernel time of the shortest calls.  fn must write preallocated buffers
+    only."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    s, e = events(torch, 2)
+    s.record()
+    for _ in range(replays):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / (replays * calls)
+    del graph
+    return ms
+
+
 def sources_sha256(root):
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
@@ -318,8 +351,10 @@ def secondary(torch, nvfp4, workloads, dev, a3, aq3):
     ra = lambda: nvfp4.kv_rope_quantize_append(kn, qk, T - Tq)
     settle(torch, ra, 0.2)
     ms_r = time_calls(torch, ra, 10, 2)
-    res["kv_rope_append"] = {"heads": H, "tokens_new": Tq, "head_dim": D, "ms": round(ms_r, 4),
-                             "GB/s": round(kn.numel() * (2 + 0.5625) / (ms_r * 1e-3) / 1e9, 1)}
+    ms_rg = time_graph(torch, ra)
+    res["kv_rope_append"] = {"heads": H, "tokens_new": Tq, "head_dim": D, "ms": round(ms_rg, 4),
+                             "GB/s": round(kn.numel() * (2 + 0.5625) / (ms_rg * 1e-3) / 1e9, 1),
+                             "timing": "HIP graph of 20 calls", "ms_eager": round(ms_r, 4)}
     del qa, oa, wsa, kn
     ms_q = time_calls(torch, lambda: nvfp4.kv_quantize(k, out=qk), 30, 2)
     ms_d = time_calls(torch, lambda: nvfp4.kv_dequantize(*qk, out=ok), 30, 2)
@@ -395,6 +430,8 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         q_ms = time_calls(torch, quant, steps, warmup)
         g_ms = time_calls(torch, gemm, steps, warmup)
         f_ms = time_calls(torch, lambda: nvfp4.gemm_fused_act(a, wq, out=cbuf, a_q=aq), steps, warmup)
+        q_ms_g = time_graph(torch, quant)
+        g_ms_g = time_graph(torch, gemm, calls=10 if flop_of(M, N, K) > 1e11 else 20)
         esz = a.element_size()
         qbytes = M * K * (2 * esz + 0.5625)
         flop = 2.0 * M * N * K
@@ -418,6 +455,9 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
             "gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(flop / (g_ms * 1e-3) / 1e12, 1),
             "gemm_frac_of_fp16_peak": round(flop / (g_ms * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
             "fused_act_ms": round(f_ms, 4), "fused_act_TFLOP/s": round(flop / (f_ms * 1e-3) / 1e12, 1),
+            "graph": {"note": "calls replayed from a HIP graph (no per-call host time)",
+                      "quantize_ms": round(q_ms_g, 4), "quantize_GB/s": round(qbytes / (q_ms_g * 1e-3) / 1e9, 1),
+                      "gemm_ms": round(g_ms_g, 4), "gemm_TFLOP/s": round(flop / (g_ms_g * 1e-3) / 1e12, 1)},
             "oracle_quantize_ms_est": round(oq_ms, 1), "oracle_gemm_ms_est": round(og_ms, 1),
             "oracle_sample_rows": rows, "oracle_threads": oracle.num_threads()}
         log("config", cfg, json.dumps(res[c["workload"]]))
@@ -476,7 +516,8 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
     kn = qa.clone()
     ra = lambda: nvfp4.kv_rope_quantize_append(kn, qk, T - Tq)
     settle(torch, ra, 0.2)
-    r_ms = time_calls(torch, ra, steps, warmup)
+    r_ms_eager = time_calls(torch, ra, steps, warmup)
+    r_ms = time_graph(torch, ra)
     nh = 1
     t0 = time.perf_counter()
     yr = oracle.rope(workloads.bf16_bits(qa_cpu[:nh]), np.arange(T - Tq, T), 10000.0)
@@ -484,6 +525,7 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
     or_ms = (time.perf_counter() - t0) * 1e3 * H / nh
     res["kv_rope_append_24x4096"] = {
         "ms": round(r_ms, 4), "GB/s": round(kn.numel() * (2 + 0.5625) / (r_ms * 1e-3) / 1e9, 1),
+        "timing": "HIP graph of 20 calls", "ms_eager": round(r_ms_eager, 4),
         "oracle_ms_est": round(or_ms, 1), "oracle_sample": "%d of %d heads" % (nh, H),
         "oracle_threads": oracle.num_threads()}
     log("rope append", json.dumps(res["kv_rope_append_24x4096"]))
