@@ -7,7 +7,9 @@ tensor whose s_g takes the exact slow path, or values on the NVFP4 grid,
 where every rounding is a tie).  Quantize, quantize along rows and dequantize
 must equal the oracle bit for bit, as must the KV-cache calls; the GEMM
 (the fast kernel or the general one, by shape) must stay within
-1e-5 * sum|a b| (+ half a bf16 ulp) of the fp64 reference everywhere."""
+1e-5 * sum|a b| (+ half a bf16 ulp) of the fp64 reference everywhere.
+Attention, the adaLN-fused quantizer and the RoPE-fused append are swept
+through the checks of their own parity tests."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +132,59 @@ def test_fuzz_kv(case):
     assert np.array_equal(codes.cpu().numpy(), oc), "case %d codes" % case
     got = deq.cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, oracle.kv_dequantize(oc, os_, oh)), "case %d round trip" % case
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_fuzz_attention(case):
+    """Random head counts, query and cache lengths, attended prefixes, query scales, softmax
+    factors (negative and zero included) and workspaces, within the bound of the attention tests
+    (which also checks that the bound stays below |ref| for most elements)."""
+    from tests.test_gpu_attention import _run as attention_run
+    rng = np.random.default_rng(13000 + case)
+    H, Tq, Tc = int(rng.integers(1, 4)), int(rng.integers(1, 400)), int(rng.integers(1, 3000))
+    T = int(rng.integers(1, Tc + 1))
+    qscale = float(rng.choice([0.5, 1.0, 3.0]))
+    scale = [None, None, -0.15, 0.0, 0.3][case % 5]
+    ws = [(None,), (0,), (None, 0)][case % 3]
+    log("fuzz attention", case, H, Tq, Tc, T, qscale, scale, ws)
+    attention_run(H, Tq, Tc, T, seed=13000 + case, qscale=qscale, scale=scale, workspaces=ws)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_adaln(case):
+    """Random row counts, widths, group sizes, eps and input dtypes for the adaLN-fused
+    quantizer, against fp64 adaLN + exact quantization with the near-boundary criterion of its
+    parity tests (both the given and the computed scale)."""
+    from tests.test_gpu_adaln import _run as adaln_run
+    rng = np.random.default_rng(15000 + case)
+    rows, k = int(rng.integers(1, 600)), 16 * int(rng.integers(1, 257))
+    rpg = int(rng.integers(1, rows + 50))
+    eps = float(rng.choice([1e-6, 1e-5, 1.0]))
+    dtype = (torch.bfloat16, torch.float32)[case % 2]
+    gen = torch.Generator().manual_seed(15000 + case)
+    x = torch.randn(rows, k, generator=gen) * torch.exp(torch.randn(1, k, generator=gen)) + \
+        torch.randn(rows, 1, generator=gen) * float(rng.choice([0.0, 1.0, 10.0]))
+    G = (rows + rpg - 1) // rpg
+    shift = torch.randn(G, k, generator=gen) * float(rng.choice([0.0, 0.3, 2.0]))
+    scale = torch.randn(G, k, generator=gen) * float(rng.choice([0.0, 0.3, 1.0]))
+    log("fuzz adaln", case, rows, k, rpg, eps, dtype)
+    adaln_run(x.to(dtype), shift, scale, rpg, eps, "fuzz %d" % case)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_fuzz_rope_append(case):
+    """Random head counts, head sizes (every one the kernel takes), cache lengths, offsets,
+    explicit or implicit positions and bases for the RoPE-fused append, against fp64 RoPE +
+    exact quantization with the near-boundary criterion of its parity tests; bytes outside the
+    appended rows must not change."""
+    from tests.test_gpu_kv_rope import _run as rope_run
+    rng = np.random.default_rng(17000 + case)
+    H = int(rng.integers(1, 5))
+    D = int(rng.choice([16, 32, 64, 128, 256, 512, 1024, 2048]))
+    Tc = int(rng.integers(1, 600 if D <= 256 else 80))
+    Tn = int(rng.integers(1, Tc + 1))
+    off = int(rng.integers(0, Tc - Tn + 1))
+    positions = rng.integers(0, 100000, Tn).astype(np.int32).tolist() if case % 2 else None
+    base = float(rng.choice([500.0, 10000.0, 1e6]))
+    log("fuzz rope", case, H, Tc, Tn, D, off, positions is not None, base)
+    rope_run(H, Tc, Tn, D, off, positions, base, seed=17000 + case, label="fuzz %d" % case)
