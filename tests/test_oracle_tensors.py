@@ -283,3 +283,37 @@ def test_kv_quantize_per_head_brute_and_structure():
         nib = brute.unpack(c[h, 2])
         for i in range(D):
             assert out[h, 2, i] == brute.dequant_bf16_bits(nib[i], s[h, 2, i // 16], hs[h])
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_quantize_brute_sweep(case):
+    """Seeded random tensors against Fraction brute force: magnitudes from 1e-20 to 1e20,
+    values on the quantization grid (every code and most scales a tie), heavy tails with
+    zeros, and given scales that make blocks saturate or underflow."""
+    rng = np.random.default_rng(500 + case)
+    rows, k = int(rng.integers(1, 5)), 16 * int(rng.integers(1, 5))
+    kind = case % 3
+    if kind == 0:
+        x = rng.standard_normal((rows, k)) * 10.0 ** float(rng.integers(-20, 21))
+    elif kind == 1:
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 6.0])
+        sv = np.array([brute.E4M3_VALUES[b] for b in range(1, 127)], dtype=object)
+        s_g = 2.0 ** float(rng.integers(-12, 4))
+        blocks = [float(sv[rng.integers(0, 126)]) for _ in range(rows * (k // 16))]
+        x = mids[rng.integers(0, len(mids), (rows, k))] * rng.choice([-1.0, 1.0], (rows, k))
+        x = x * np.repeat(np.array(blocks).reshape(rows, k // 16), 16, axis=1) * s_g
+    else:
+        x = rng.standard_normal((rows, k))
+        x[rng.random((rows, k)) < 0.05] *= 1000.0
+        x[rng.random((rows, k)) < 0.2] = 0.0
+    x = x.astype(np.float32)
+    if case % 4 == 3:  # a given scale at a random multiple of the computed one
+        g = np.float32(oracle.global_scale(oracle.amax(x)) * float(rng.choice([0.01, 0.3, 2.0, 50.0])))
+        codes, scales, s_g = oracle.quantize(x, s_g=g)
+        bc, bs, bg = brute.quantize([[float(v) for v in r] for r in x], s_g=float(g))
+        assert float(s_g) == float(g)
+        for r in range(rows):
+            assert list(scales[r]) == bs[r]
+            assert list(codes[r]) == brute.pack(bc[r])
+    else:
+        _check_vs_brute(x)
