@@ -629,35 +629,51 @@ __device__ __forceinline__ void fast_decode_first(FastPipe<FN>& P) {
 #define NVFP4_DEC_PAIR(O, W, S, SEL, OPS)                                          \
   "v_cvt_scalef32_pk_f16_fp4 %[" O "], %[" W "], 1.0" SEL "\n\t"                  \
   "v_pk_mul_f16 %[" O "], %[" S "], %[" O "]" OPS "\n\t"
-#define NVFP4_MFMA(C) "v_mfma_f32_32x32x16_f16 %[" C "], %[b], %[a" C "], %[" C "]\n\t"
+// op_sel of the scale multiply: the fp16 scale of block 2q (LO) or 2q + 1 (HI)
+// of the scale pair, broadcast to both halves.
+#define NVFP4_OPS_LO " op_sel:[0,0] op_sel_hi:[0,1]"
+#define NVFP4_OPS_HI " op_sel:[1,0] op_sel_hi:[1,1]"
+#define NVFP4_MFMA_ACC(C) "v_mfma_f32_32x32x16_f16 %[" C "], %[b], %[a" C "], %[" C "]\n\t"
+#define NVFP4_MFMA_ZERO(C) "v_mfma_f32_32x32x16_f16 %[" C "], %[b], %[a" C "], 0\n\t"
+// Both forms of a block in one asm statement, chosen by the wave-uniform
+// operand z (nonzero: zero accumulator), so that the accumulators stay tied
+// to the same registers on both paths.
+#define NVFP4_EITHER(BODY_ZERO, BODY_ACC)                                         \
+  "s_cmp_lg_u32 %[z], 0\n\ts_cbranch_scc0 .Lacc%=\n\t" BODY_ZERO "s_branch .Lend%=\n" \
+  ".Lacc%=:\n\t" BODY_ACC ".Lend%=:\n\t"
 
-template <bool kHi>
+template <bool kHi, bool kMaybeZero>
 __device__ __forceinline__ void mfma4_decode2(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const f16x8& b,
                                               const f16x8 (&a)[4], uint32_t wx, uint32_t sx, uint32_t wy,
-                                              uint32_t sy, f16x8& ox, f16x8& oy) {
+                                              uint32_t sy, f16x8& ox, f16x8& oy, uint32_t zero) {
   uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-#define NVFP4_BODY(OPS)                                                                              \
-  "s_nop 1\n\t" NVFP4_MFMA("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                           \
-      NVFP4_DEC_PAIR("x1", "wx", "sx", " op_sel:[1,0,0]", OPS) NVFP4_MFMA("c1")                      \
+#define NVFP4_BODY(OPS, MF)                                                                          \
+  "s_nop 1\n\t" MF("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                                   \
+      NVFP4_DEC_PAIR("x1", "wx", "sx", " op_sel:[1,0,0]", OPS) MF("c1")                              \
       NVFP4_DEC_PAIR("x2", "wx", "sx", " op_sel:[0,1,0]", OPS)                                       \
-      NVFP4_DEC_PAIR("x3", "wx", "sx", " op_sel:[1,1,0]", OPS) NVFP4_MFMA("c2")                      \
+      NVFP4_DEC_PAIR("x3", "wx", "sx", " op_sel:[1,1,0]", OPS) MF("c2")                              \
       NVFP4_DEC_PAIR("y0", "wy", "sy", "", OPS) NVFP4_DEC_PAIR("y1", "wy", "sy", " op_sel:[1,0,0]", OPS) \
-      NVFP4_MFMA("c3") NVFP4_DEC_PAIR("y2", "wy", "sy", " op_sel:[0,1,0]", OPS)                      \
+      MF("c3") NVFP4_DEC_PAIR("y2", "wy", "sy", " op_sel:[0,1,0]", OPS)                              \
       NVFP4_DEC_PAIR("y3", "wy", "sy", " op_sel:[1,1,0]", OPS)
-  if constexpr (kHi) {
-    asm volatile(NVFP4_BODY(" op_sel:[1,0] op_sel_hi:[1,1]")
-                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
-                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3)
-                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
-                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy));
-  } else {
-    asm volatile(NVFP4_BODY(" op_sel:[0,0] op_sel_hi:[0,1]")
-                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
-                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3)
-                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
-                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy));
-  }
+#define NVFP4_OUT2                                                                                         \
+  [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1), [x2] "=&v"(x2), \
+      [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3)
+#define NVFP4_IN2                                                                                          \
+  [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx), [sx] "v"(sx), \
+      [wy] "v"(wy), [sy] "v"(sy)
+  if constexpr (kHi && kMaybeZero)
+    asm volatile(NVFP4_EITHER(NVFP4_BODY(NVFP4_OPS_HI, NVFP4_MFMA_ZERO), NVFP4_BODY(NVFP4_OPS_HI, NVFP4_MFMA_ACC))
+                 : NVFP4_OUT2 : NVFP4_IN2, [z] "s"(zero) : "scc");
+  else if constexpr (kHi)
+    asm volatile(NVFP4_BODY(NVFP4_OPS_HI, NVFP4_MFMA_ACC) : NVFP4_OUT2 : NVFP4_IN2);
+  else if constexpr (kMaybeZero)
+    asm volatile(NVFP4_EITHER(NVFP4_BODY(NVFP4_OPS_LO, NVFP4_MFMA_ZERO), NVFP4_BODY(NVFP4_OPS_LO, NVFP4_MFMA_ACC))
+                 : NVFP4_OUT2 : NVFP4_IN2, [z] "s"(zero) : "scc");
+  else
+    asm volatile(NVFP4_BODY(NVFP4_OPS_LO, NVFP4_MFMA_ACC) : NVFP4_OUT2 : NVFP4_IN2);
 #undef NVFP4_BODY
+#undef NVFP4_OUT2
+#undef NVFP4_IN2
   ox = __builtin_bit_cast(f16x8, u32x4{x0, x1, x2, x3});
   oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
 }
@@ -667,38 +683,42 @@ __device__ __forceinline__ void mfma4_decode2(f32x16& c0, f32x16& c1, f32x16& c2
 // tile, which decodes the next step's 3 B frags.  The hazard rules above
 // hold: the outputs' last MFMA readers are the previous step's blocks, and
 // their first readers come in the next step's blocks, after its s_nop.
-template <bool kHi>
+template <bool kHi, bool kMaybeZero>
 __device__ __forceinline__ void mfma4_decode3(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3, const f16x8& b,
                                               const f16x8 (&a)[4], uint32_t wx, uint32_t sx, uint32_t wy,
                                               uint32_t sy, uint32_t wz, uint32_t sz, f16x8& ox, f16x8& oy,
-                                              f16x8& oz) {
+                                              f16x8& oz, uint32_t zero) {
   uint32_t x0, x1, x2, x3, y0, y1, y2, y3, z0, z1, z2, z3;
-#define NVFP4_BODY3(OPS)                                                                                  \
-  "s_nop 1\n\t" NVFP4_MFMA("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                                \
+#define NVFP4_BODY3(OPS, MF)                                                                              \
+  "s_nop 1\n\t" MF("c0") NVFP4_DEC_PAIR("x0", "wx", "sx", "", OPS)                                        \
       NVFP4_DEC_PAIR("x1", "wx", "sx", " op_sel:[1,0,0]", OPS)                                            \
-      NVFP4_DEC_PAIR("x2", "wx", "sx", " op_sel:[0,1,0]", OPS) NVFP4_MFMA("c1")                           \
+      NVFP4_DEC_PAIR("x2", "wx", "sx", " op_sel:[0,1,0]", OPS) MF("c1")                                   \
       NVFP4_DEC_PAIR("x3", "wx", "sx", " op_sel:[1,1,0]", OPS) NVFP4_DEC_PAIR("y0", "wy", "sy", "", OPS)  \
-      NVFP4_DEC_PAIR("y1", "wy", "sy", " op_sel:[1,0,0]", OPS) NVFP4_MFMA("c2")                           \
+      NVFP4_DEC_PAIR("y1", "wy", "sy", " op_sel:[1,0,0]", OPS) MF("c2")                                   \
       NVFP4_DEC_PAIR("y2", "wy", "sy", " op_sel:[0,1,0]", OPS)                                            \
       NVFP4_DEC_PAIR("y3", "wy", "sy", " op_sel:[1,1,0]", OPS) NVFP4_DEC_PAIR("z0", "wz", "sz", "", OPS)  \
-      NVFP4_MFMA("c3") NVFP4_DEC_PAIR("z1", "wz", "sz", " op_sel:[1,0,0]", OPS)                           \
+      MF("c3") NVFP4_DEC_PAIR("z1", "wz", "sz", " op_sel:[1,0,0]", OPS)                                   \
       NVFP4_DEC_PAIR("z2", "wz", "sz", " op_sel:[0,1,0]", OPS) NVFP4_DEC_PAIR("z3", "wz", "sz", " op_sel:[1,1,0]", OPS)
-  if constexpr (kHi) {
-    asm volatile(NVFP4_BODY3(" op_sel:[1,0] op_sel_hi:[1,1]")
-                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
-                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3),
-                   [z0] "=&v"(z0), [z1] "=&v"(z1), [z2] "=&v"(z2), [z3] "=&v"(z3)
-                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
-                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy), [wz] "v"(wz), [sz] "v"(sz));
-  } else {
-    asm volatile(NVFP4_BODY3(" op_sel:[0,0] op_sel_hi:[0,1]")
-                 : [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1),
-                   [x2] "=&v"(x2), [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3),
-                   [z0] "=&v"(z0), [z1] "=&v"(z1), [z2] "=&v"(z2), [z3] "=&v"(z3)
-                 : [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx),
-                   [sx] "v"(sx), [wy] "v"(wy), [sy] "v"(sy), [wz] "v"(wz), [sz] "v"(sz));
-  }
+#define NVFP4_OUT3                                                                                         \
+  [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3), [x0] "=&v"(x0), [x1] "=&v"(x1), [x2] "=&v"(x2), \
+      [x3] "=&v"(x3), [y0] "=&v"(y0), [y1] "=&v"(y1), [y2] "=&v"(y2), [y3] "=&v"(y3), [z0] "=&v"(z0),         \
+      [z1] "=&v"(z1), [z2] "=&v"(z2), [z3] "=&v"(z3)
+#define NVFP4_IN3                                                                                          \
+  [b] "v"(b), [ac0] "v"(a[0]), [ac1] "v"(a[1]), [ac2] "v"(a[2]), [ac3] "v"(a[3]), [wx] "v"(wx), [sx] "v"(sx), \
+      [wy] "v"(wy), [sy] "v"(sy), [wz] "v"(wz), [sz] "v"(sz)
+  if constexpr (kHi && kMaybeZero)
+    asm volatile(NVFP4_EITHER(NVFP4_BODY3(NVFP4_OPS_HI, NVFP4_MFMA_ZERO), NVFP4_BODY3(NVFP4_OPS_HI, NVFP4_MFMA_ACC))
+                 : NVFP4_OUT3 : NVFP4_IN3, [z] "s"(zero) : "scc");
+  else if constexpr (kHi)
+    asm volatile(NVFP4_BODY3(NVFP4_OPS_HI, NVFP4_MFMA_ACC) : NVFP4_OUT3 : NVFP4_IN3);
+  else if constexpr (kMaybeZero)
+    asm volatile(NVFP4_EITHER(NVFP4_BODY3(NVFP4_OPS_LO, NVFP4_MFMA_ZERO), NVFP4_BODY3(NVFP4_OPS_LO, NVFP4_MFMA_ACC))
+                 : NVFP4_OUT3 : NVFP4_IN3, [z] "s"(zero) : "scc");
+  else
+    asm volatile(NVFP4_BODY3(NVFP4_OPS_LO, NVFP4_MFMA_ACC) : NVFP4_OUT3 : NVFP4_IN3);
 #undef NVFP4_BODY3
+#undef NVFP4_OUT3
+#undef NVFP4_IN3
   ox = __builtin_bit_cast(f16x8, u32x4{x0, x1, x2, x3});
   oy = __builtin_bit_cast(f16x8, u32x4{y0, y1, y2, y3});
   oz = __builtin_bit_cast(f16x8, u32x4{z0, z1, z2, z3});
@@ -712,9 +732,9 @@ __device__ __forceinline__ void mfma4_decode3(f32x16& c0, f32x16& c1, f32x16& c2
 // workgroup that decode works on stale registers and is never used.  With
 // FN = 4 blocks 0-1 decode the next step's A frags and blocks 2-3 its B
 // frags; with FN = 3 block 2 decodes all three B frags.
-template <int n, int FN>
+template <int n, int FN, bool kMaybeZero = false>
 __device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& P, f32x16 (&acc)[FN][4],
-                                          const FastLane& L, const FastRefill<FN>& rf) {
+                                          const FastLane& L, const FastRefill<FN>& rf, uint32_t zero = 0) {
   // copies of the refill after every kRefillEvery-th MFMA block from step kRefillStep on (3 or 4 blocks a step)
   constexpr int kBlocks = FN == 4 ? 4 : 3;
   constexpr int j0 = (n - kRefillStep) * kBlocks;  // MFMA block index from the first refill step
@@ -728,24 +748,24 @@ __device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& 
   constexpr bool hi = t1 >= 2;
   const uint4* A = P.ca[u1];
   const uint4* B = P.cb[u1];
-  mfma4_decode2<hi>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
-                    word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1]);
+  mfma4_decode2<hi, kMaybeZero>(acc[0][0], acc[0][1], acc[0][2], acc[0][3], P.bv[c][0], P.av[c], word_of(A[0], t1), P.sa[u1][0],
+                    word_of(A[1], t1), P.sa[u1][1], P.av[x][0], P.av[x][1], zero);
   if constexpr (n >= kRefillStep && (j0 + 0) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 0) / kRefillEvery>();
-  mfma4_decode2<hi>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
-                    word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3]);
+  mfma4_decode2<hi, kMaybeZero>(acc[1][0], acc[1][1], acc[1][2], acc[1][3], P.bv[c][1], P.av[c], word_of(A[2], t1), P.sa[u1][2],
+                    word_of(A[3], t1), P.sa[u1][3], P.av[x][2], P.av[x][3], zero);
   if constexpr (n >= kRefillStep && (j0 + 1) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 1) / kRefillEvery>();
   if constexpr (FN == 4) {
-    mfma4_decode2<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
-                      word_of(B[1], t1), P.sb[u1][1], P.bv[x][0], P.bv[x][1]);
+    mfma4_decode2<hi, kMaybeZero>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
+                      word_of(B[1], t1), P.sb[u1][1], P.bv[x][0], P.bv[x][1], zero);
     if constexpr (n >= kRefillStep && (j0 + 2) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 2) / kRefillEvery>();
-    mfma4_decode2<hi>(acc[3][0], acc[3][1], acc[3][2], acc[3][3], P.bv[c][3], P.av[c], word_of(B[2], t1), P.sb[u1][2],
-                      word_of(B[3], t1), P.sb[u1][3], P.bv[x][2], P.bv[x][3]);
+    mfma4_decode2<hi, kMaybeZero>(acc[3][0], acc[3][1], acc[3][2], acc[3][3], P.bv[c][3], P.av[c], word_of(B[2], t1), P.sb[u1][2],
+                      word_of(B[3], t1), P.sb[u1][3], P.bv[x][2], P.bv[x][3], zero);
     if constexpr (n >= kRefillStep && (j0 + 3) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 3) / kRefillEvery>();
   } else {
     static_assert(FN == 3, "FN is 3 or 4");
-    mfma4_decode3<hi>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
+    mfma4_decode3<hi, kMaybeZero>(acc[2][0], acc[2][1], acc[2][2], acc[2][3], P.bv[c][2], P.av[c], word_of(B[0], t1), P.sb[u1][0],
                       word_of(B[1], t1), P.sb[u1][1], word_of(B[2], t1), P.sb[u1][2], P.bv[x][0], P.bv[x][1],
-                      P.bv[x][2]);
+                      P.bv[x][2], zero);
     if constexpr (n >= kRefillStep && (j0 + 2) % kRefillEvery == 0) rf.template copy<kRefillBurst + (j0 + 2) / kRefillEvery>();
   }
 }
@@ -753,19 +773,20 @@ __device__ __forceinline__ void fast_step(const FastStage<FN>& S, FastPipe<FN>& 
 static_assert(kBarrierStep >= 8 && kBarrierStep <= 11, "S is last read at step 8; Sn is first read at step 12");
 static_assert(kRefillStep > kBarrierStep, "copies into S only after the barrier");
 
-template <int n, int FN>
+template <int n, int FN, bool kMaybeFirst>
 __device__ __forceinline__ void fast_stage_steps(const FastStage<FN>& S, const FastStage<FN>& Sn, FastPipe<FN>& P,
-                                                 f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf) {
+                                                 f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf,
+                                                 uint32_t first) {
   if constexpr (n < 16) {
     if constexpr (n == 12) fast_read_sub(Sn, P, 0, L, 0);
-    fast_step<n>(S, P, acc, L, rf);
+    fast_step<n, FN, kMaybeFirst && n == 0>(S, P, acc, L, rf, first);
     if constexpr (n == kBarrierStep) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       rf.whole_stage();
       rf.template burst<kRefillBurst>();
     }
-    fast_stage_steps<n + 1>(S, Sn, P, acc, L, rf);
+    fast_stage_steps<n + 1, FN, kMaybeFirst>(S, Sn, P, acc, L, rf, first);
   }
 }
 
@@ -776,14 +797,18 @@ __device__ __forceinline__ void fast_stage_steps(const FastStage<FN>& S, const F
 // part at once and the rest between the MFMA blocks of the following steps,
 // and sub-chunk 0 of Sn is read at step 12 for the decode carried by step 15
 // (after the last stage of a workgroup Sn holds stale data, read but never
-// used).
-template <int FN>
+// used).  In a tile's first stage (kMaybeFirst and `first` nonzero) the
+// MFMAs of step 0 take a zero accumulator (an inline 0 as their C operand),
+// which starts every output tile of the wave without writing 256 zeros to
+// the accumulators first.
+template <bool kMaybeFirst, int FN>
 __device__ __forceinline__ void fast_stage(const FastStage<FN>& S, const FastStage<FN>& Sn, FastPipe<FN>& P,
-                                           f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf) {
+                                           f32x16 (&acc)[FN][4], const FastLane& L, const FastRefill<FN>& rf,
+                                           uint32_t first) {
   constexpr int kBlocks = FN == 4 ? 4 : 3;
   static_assert(kRefillBurst + (16 - kRefillStep) * kBlocks / kRefillEvery >= FastRefill<FN>::kCopies,
                 "every copy of the refill is issued within the stage");
-  fast_stage_steps<0>(S, Sn, P, acc, L, rf);
+  fast_stage_steps<0, FN, kMaybeFirst>(S, Sn, P, acc, L, rf, first);
 }
 
 // Epilogue of one tile: lane (r, h), accumulator element e of MFMA tile (j, i)
@@ -796,10 +821,15 @@ __device__ __forceinline__ void fast_stage(const FastStage<FN>& S, const FastSta
 // VGPRs ahead of the full/edge branch (both paths read them), runs out of
 // VGPRs and spills; the reloads then wait, since vmcnt also counts stores,
 // for every output store issued before them.
-__device__ __forceinline__ f32x16 pinned(const f32x16& acc) {
-  f32x16 a = acc;
-  asm volatile("" : "+a"(a));
-  return a;
+__device__ __forceinline__ f32x16 pinned(f32x16& acc) {
+  f32x16 v;
+#pragma unroll
+  for (int e = 0; e < 16; e++) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(acc[e]));
+    v[e] = x;
+  }
+  return v;
 }
 
 template <bool kBf16Out>
@@ -816,7 +846,7 @@ __device__ __forceinline__ void fast_store4(void* __restrict__ c, int64_t idx, c
 
 // Tiles that cross row M or column N: every store checks its row and column.
 template <bool kBf16Out, int FN>
-__device__ __forceinline__ void fast_epilogue_edge(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
+__device__ __forceinline__ void fast_epilogue_edge(f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
                                                    int64_t n0, int M, int N, int wm, int wn, int r, int h, float g) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -849,7 +879,7 @@ __device__ __forceinline__ uint32_t bf16_pair(const f32x16& a, int gq, int e, fl
 // or 16 rows (NJ = 1: 64 contiguous bytes per row).  `dst0` is the output
 // element of row 0, column 32 j0 of the run.
 template <int NJ, int FN>
-__device__ __forceinline__ void bf16_run(const f32x16 (&acc)[FN][4], int i, int j0, __bf16* __restrict__ dst0,
+__device__ __forceinline__ void bf16_run(f32x16 (&acc)[FN][4], int i, int j0, __bf16* __restrict__ dst0,
                                          uint32_t N, int r, int h, float g, uint8_t* wl) {
   const int lane = threadIdx.x & 63;
   const uint32_t wsw = (uint32_t)((r >> 1) & 7);
@@ -880,7 +910,7 @@ __device__ __forceinline__ void bf16_run(const f32x16 (&acc)[FN][4], int i, int 
 // 0-95 of the tile (frags 0-1 paired, frag 2 alone) and wave 1 columns 96-191
 // (frag 0 alone, frags 1-2 paired): the two single frags share one line.
 template <int FN>
-__device__ __forceinline__ void fast_epilogue_full_bf16(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
+__device__ __forceinline__ void fast_epilogue_full_bf16(f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
                                                         int64_t n0, int N, int wm, int wn, int r, int h, float g,
                                                         uint8_t* wl) {
   const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128), col0 = (uint32_t)n0 + (uint32_t)(wn * 32 * FN);
@@ -902,7 +932,7 @@ __device__ __forceinline__ void fast_epilogue_full_bf16(const f32x16 (&acc)[FN][
 
 // Full tiles, fp32 output: 16-byte stores straight from the MFMA layout.
 template <int FN>
-__device__ __forceinline__ void fast_epilogue_full_f32(const f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
+__device__ __forceinline__ void fast_epilogue_full_f32(f32x16 (&acc)[FN][4], void* __restrict__ c, int64_t m0,
                                                        int64_t n0, int N, int wm, int wn, int r, int h, float g) {
   const uint32_t row0 = (uint32_t)m0 + (uint32_t)(wm * 128 + r);
   const uint32_t col0 = (uint32_t)n0 + (uint32_t)(wn * 32 * FN + 4 * h);
@@ -944,7 +974,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
   const float g = a_sg[0] * b_sg[0];
   const bool small_c = (int64_t)M * N < (int64_t(1) << 32);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches on wn
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5;
 
@@ -989,11 +1020,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
     if (has_next) tile_of_lin(lin + G, tiles_m, tiles_n, tm_next, tn_next);
     const bool edge_next = (int64_t)(tm_next + 1) * kTile > M || (int64_t)(tn_next + 1) * kTN > N;
     const int64_t m0_next = (int64_t)tm_next * kTile, n0_next = (int64_t)tn_next * kTN;
+    // Not zeroed: the first k16-step of the tile writes every accumulator
+    // with zero-C MFMAs (nk >= 2, so every tile runs that step).  The empty
+    // asm statements give them a defined value without any instruction (left
+    // undefined, the register allocator spills around the tile loop).
     f32x16 acc[FN][4];
 #pragma unroll
     for (int j = 0; j < FN; j++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[j][i] = f32x16{};
+      for (int i = 0; i < 4; i++) asm volatile("" : "=a"(acc[j][i]));
     for (int kc = 0; kc < nk; kc += 2) {
       // stage kc (st0), then kc + 1 (st1); each refills its LDS stage with
       // the stage two later: kc + 2 of this tile or, at the end of the tile,
@@ -1003,10 +1038,13 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_fast_kernel(
       const int64_t rm0 = more ? m0 : m0_next, rn0 = more ? n0 : n0_next;
       const bool redge = more ? edge : edge_next, ron = more || has_next;
       const int rkc = more ? kc + 2 : 0;
-      fast_stage(st0, st1, P, acc, L,
-                 FastRefill<FN>(lds0, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K, rkc));
-      fast_stage(st1, st0, P, acc, L,
-                 FastRefill<FN>(lds1, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K, rkc + 1));
+      fast_stage<true>(st0, st1, P, acc, L,
+                       FastRefill<FN>(lds0, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K, rkc),
+                       __builtin_amdgcn_readfirstlane(kc == 0 ? 1u : 0u));
+      fast_stage<false>(st1, st0, P, acc, L,
+                        FastRefill<FN>(lds1, ld, ron, redge, a_codes, a_scales, b_codes, b_scales, rm0, rn0, M, N, K,
+                                       rkc + 1),
+                        0u);
     }
     // The stores drain while the next tile computes (the next wait comes
     // 12 k16-steps later).
@@ -1034,7 +1072,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   const bool fast = (K % kKC == 0) && ((uintptr_t)a_codes % 16 == 0) && ((uintptr_t)b_codes % 16 == 0) &&
                     ((uintptr_t)a_scales % 8 == 0) && ((uintptr_t)b_scales % 8 == 0);
   const bool bf = c_dtype == kDtypeBf16;
-  const bool dma = (K % (2 * kFastKC) == 0) && (N % 4 == 0) && (M * (K / 2) < (int64_t(1) << 32)) &&
+  const bool dma = K > 0 && (K % (2 * kFastKC) == 0) && (N % 4 == 0) && (M * (K / 2) < (int64_t(1) << 32)) &&
                    (N * (K / 2) < (int64_t(1) << 32)) && ((uintptr_t)a_codes % 16 == 0) &&
                    ((uintptr_t)b_codes % 16 == 0) && ((uintptr_t)a_scales % 16 == 0) &&
                    ((uintptr_t)b_scales % 16 == 0) && ((uintptr_t)c % 16 == 0);
