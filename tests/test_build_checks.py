@@ -189,22 +189,35 @@ def test_attention_split_choice():
     assert 0 < b // per(1, 1) <= 32
 
 
+_GEMM_ASM = {}
+
+
+def _gemm_asm():
+    """gfx950 assembly of nvfp4_gemm.hip (compiled once per session)."""
+    if "asm" not in _GEMM_ASM:
+        src = os.path.join(ROOT, "long_video_dit_amd", "csrc", "nvfp4_gemm.hip")
+        with tempfile.TemporaryDirectory() as d:
+            out = os.path.join(d, "gemm.s")
+            r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-O3",
+                                "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", src,
+                                "-o", out], capture_output=True, text=True)
+            if r.returncode != 0:
+                pytest.fail(r.stderr[-2000:])
+            _GEMM_ASM["asm"] = open(out).read()
+    return _GEMM_ASM["asm"]
+
+
+def _fast_kernel_bodies():
+    asm = _gemm_asm()
+    kernels = re.findall(r"^(_Z\S*fast_kernel\S*):", asm, re.M)
+    assert kernels
+    return {k: asm[asm.index(k + ":"):asm.index(".Lfunc_end", asm.index(k + ":"))] for k in kernels}
+
+
 def test_gemm_fast_path_leaves_m0_to_the_lds_copies():
     """The fast GEMM kernel sets M0 inside its own asm statements; the compiler
     must not keep any value of its own in M0 in that kernel."""
-    src = os.path.join(ROOT, "long_video_dit_amd", "csrc", "nvfp4_gemm.hip")
-    with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "gemm.s")
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-O3", "-std=c++17",
-                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", src, "-o", out],
-                           capture_output=True, text=True)
-        if r.returncode != 0:
-            pytest.fail(r.stderr[-2000:])
-        asm = open(out).read()
-    kernels = re.findall(r"^(_Z\S*fast_kernel\S*):", asm, re.M)
-    assert kernels
-    for k in kernels:
-        body = asm[asm.index(k + ":"):asm.index(".Lfunc_end", asm.index(k + ":"))]
+    for k, body in _fast_kernel_bodies().items():
         inside = False
         for line in body.splitlines():
             if ";;#ASMSTART" in line:
@@ -213,6 +226,24 @@ def test_gemm_fast_path_leaves_m0_to_the_lds_copies():
                 inside = False
             elif not inside:
                 assert not re.search(r"\bm0\b", line.split(";")[0]), (k, line)
+
+
+def test_gemm_fast_path_accumulators_stay_in_place():
+    """The 256 x 256 fast kernels start each tile with zero-accumulator MFMAs
+    (an inline 0 as the C operand, chosen in the asm by a scalar compare of an
+    SGPR flag) and read the accumulators in place in the epilogue: no
+    accumulator zero-writes, no accumulator-to-accumulator copies, and no
+    spills, in every fast kernel."""
+    bodies = _fast_kernel_bodies()
+    for k, body in bodies.items():
+        assert "scratch_" not in body, k
+        assert not re.search(r"s_cmp_lg_u32 v", body), k  # the flag of the zero-C branch must be an SGPR
+        assert len(re.findall(r"v_mfma_f32_32x32x16_f16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], 0$", body, re.M)) > 0, k
+        assert "v_accvgpr_mov" not in body, k
+    full = [k for k in bodies if "Li4E" in k]
+    assert len(full) == 2  # bf16 and fp32 output
+    for k in full:
+        assert "v_accvgpr_write" not in bodies[k], k
 
 
 def test_binding_rejects_mismatched_operands():
