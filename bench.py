@@ -106,6 +106,28 @@ def time_calls(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def time_calls_dist(torch, fn, steps, warmup):
+    """Per-call ms of fn() over `steps` calls, an HIP event pair around each
+    call on the current stream: (mean, p10, median, p90)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pairs = [events(torch, 2) for _ in range(steps)]
+    for s, e in pairs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return dist([s.elapsed_time(e) for s, e in pairs])
+
+
+def dist(ms):
+    """(mean, p10, median, p90) of a list of times, rounded to 0.1 us."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return tuple(round(float(v), 4) for v in (a.mean(), *np.percentile(a, [10, 50, 90])))
+
+
 def flop_of(M, N, K):
     return 2.0 * M * N * K
 
@@ -216,7 +238,9 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = sum(s.elapsed_time(e) for s, e in zip(gemm_s, gemm_e)) / args.steps
+    gemm_times = [s.elapsed_time(e) for s, e in zip(gemm_s, gemm_e)]
+    gemm_ms = sum(gemm_times) / args.steps
+    _, gemm_p10, gemm_p50, gemm_p90 = dist(gemm_times)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (gemm_ms * 1e-3) / 1e12
 
@@ -239,7 +263,7 @@ def main():
                      "peak": MFMA_PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": gemm_traffic(root),
                      "algorithmic_bytes": M * (K // 2 + K // 16) + N * (K // 2 + K // 16) + 2 * M * N + 8,
-                     "gemm_ms": round(gemm_ms, 4)},
+                     "gemm_ms": round(gemm_ms, 4), "gemm_ms_p10_p50_p90": [gemm_p10, gemm_p50, gemm_p90]},
     }
     log("step %.3f ms, gemm %.3f ms -> %.1f TFLOP/s step, %.1f TFLOP/s gemm" % (ms_per_step, gemm_ms, value,
                                                                              achieved))
@@ -427,8 +451,8 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         gemm = lambda: nvfp4.gemm(aq, wq, out=cbuf)
         quant()
         settle(torch, gemm)
-        q_ms = time_calls(torch, quant, steps, warmup)
-        g_ms = time_calls(torch, gemm, steps, warmup)
+        q_ms, *q_pct = time_calls_dist(torch, quant, steps, warmup)
+        g_ms, *g_pct = time_calls_dist(torch, gemm, steps, warmup)
         f_ms = time_calls(torch, lambda: nvfp4.gemm_fused_act(a, wq, out=cbuf, a_q=aq), steps, warmup)
         q_ms_g = time_graph(torch, quant)
         g_ms_g = time_graph(torch, gemm, calls=10 if flop_of(M, N, K) > 1e11 else 20)
@@ -452,7 +476,9 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         res[c["workload"]] = {
             "M": M, "N": N, "K": K, "a_dtype": c["a_dtype"], "c_dtype": c["c_dtype"],
             "quantize_ms": round(q_ms, 4), "quantize_GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_ms_p10_p50_p90": q_pct,
             "gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(flop / (g_ms * 1e-3) / 1e12, 1),
+            "gemm_ms_p10_p50_p90": g_pct,
             "gemm_frac_of_fp16_peak": round(flop / (g_ms * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 4),
             "fused_act_ms": round(f_ms, 4), "fused_act_TFLOP/s": round(flop / (f_ms * 1e-3) / 1e12, 1),
             "graph": {"note": "calls replayed from a HIP graph (no per-call host time)",
@@ -477,7 +503,7 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         nvfp4.kv_dequantize(*qv, out=ov)
 
     settle(torch, rt)
-    rt_ms = time_calls(torch, rt, steps, warmup)
+    rt_ms, *rt_pct = time_calls_dist(torch, rt, steps, warmup)
     n = 2 * k.numel()
     kb = workloads.bf16_bits(k_cpu[:1])
     t0 = time.perf_counter()
@@ -485,6 +511,7 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
     oracle.kv_dequantize(oc, os_, oh)
     o_ms = (time.perf_counter() - t0) * 1e3 * 2 * H
     res[c["workload"]] = {"H": H, "T": T, "D": D, "tensors": 2, "roundtrip_ms": round(rt_ms, 4),
+                          "roundtrip_ms_p10_p50_p90": rt_pct,
                           "roundtrip_GB/s": round(n * (B_AMAX + B_ENCODE + B_DEQUANT) / (rt_ms * 1e-3) / 1e9, 1),
                           "oracle_roundtrip_ms_est": round(o_ms, 1), "oracle_sample": "1 head of K",
                           "oracle_threads": oracle.num_threads()}
