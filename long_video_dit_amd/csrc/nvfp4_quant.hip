@@ -548,7 +548,7 @@ template <typename T>
 __device__ __forceinline__ void load4(const T* __restrict__ p, float (&f)[4]);
 template <>
 __device__ __forceinline__ void load4<uint16_t>(const uint16_t* __restrict__ p, float (&f)[4]) {
-  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   f[0] = __uint_as_float(v.x << 16);
   f[1] = __uint_as_float(v.x & 0xffff0000u);
   f[2] = __uint_as_float(v.y << 16);
@@ -556,7 +556,7 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* __restrict__ p, 
 }
 template <>
 __device__ __forceinline__ void load4<float>(const float* __restrict__ p, float (&f)[4]) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   f[0] = v.x;
   f[1] = v.y;
   f[2] = v.z;
@@ -655,14 +655,16 @@ __global__ __launch_bounds__(kTThreads) void encode_t_kernel(const T* __restrict
     }
     __syncthreads();
   }
-  // Codes: 16 lanes per column, lane p stores rows 16 p .. 16 p + 15 (8 B).
+  // Codes: 16 lanes per column, lane p stores rows 16 p .. 16 p + 15 (8 B),
+  // non-temporal like the tile's loads (x is streamed once; the codes are
+  // whole 128-byte lines).
   const int64_t words_per_col = rows / 8;
 #pragma unroll
   for (int it = 0; it < kTC * 16 / kTThreads; it++) {
     const int idx = it * kTThreads + threadIdx.x, cl = idx >> 4, p = idx & 15;
     if (tc0 + cl < cols && tr0 + 16 * p < rows)
-      *reinterpret_cast<u32x2*>(codes + (tc0 + cl) * words_per_col + tr0 / 8 + 2 * p) =
-          *reinterpret_cast<const u32x2*>(&sc[cl][2 * p]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x2*>(&sc[cl][2 * p]),
+                                  reinterpret_cast<u32x2*>(codes + (tc0 + cl) * words_per_col + tr0 / 8 + 2 * p));
   }
   // Scale bytes: 4 lanes per column, 4 bytes each when aligned.
   {
