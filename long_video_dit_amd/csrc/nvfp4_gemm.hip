@@ -361,12 +361,14 @@ constexpr int kFastKC = 256;  // K per LDS stage of the fast path: 128 code byte
 // Where a stage's refill goes (see fast_stage): the waves synchronize after
 // k16-step kBarrierStep, kRefillBurst copies follow at once, and the rest come
 // one after every kRefillEvery-th MFMA block from step kRefillStep on.  On the
-// FFN shapes this is ~2% faster than issuing all copies at the barrier; the
-// matrix cores lose less time to the CU's address unit.
+// FFN shapes this is ~2.5% faster than issuing all copies at the barrier; the
+// matrix cores lose less time to the CU's address unit.  (6 at once and one
+// after every block measured 0.5-0.7% faster than 10 at once and one after
+// every other block, with the zero-accumulator tile start.)
 constexpr int kBarrierStep = 11;
 constexpr int kRefillStep = 12;
-constexpr int kRefillBurst = 10;
-constexpr int kRefillEvery = 2;
+constexpr int kRefillBurst = 6;
+constexpr int kRefillEvery = 1;
 
 // The fast path's output tile is 256 rows of A by 64 FN rows of B: each of
 // the 4 waves (2 x 2) holds 128 rows x 32 FN columns, FN = 4 (256 x 256) or
