@@ -44,7 +44,7 @@ GEMM_SOURCES = ("long_video_dit_amd/csrc/nvfp4_gemm.hip", "long_video_dit_amd/cs
 # HBM byte counters of one GEMM launch (FFN up-projection, bf16 out), KiB per dispatch, and the
 # factors that map them to bytes (a 1 GiB copy reads FETCH_SIZE = 512 MiB, WRITE_SIZE = 1 GiB).
 # Taken with profiles/gemm_w4a4_fast_kernel_ffn_up_16384x14336x3072.md's commands.
-GEMM_COUNTERS = {"sources_sha256": "d88aa99bd6873d4890c58c776ae26c23cc3717b4f50e5e6830263af2dd68ddb7",
+GEMM_COUNTERS = {"sources_sha256": "fa4ee1ae5d532974c8c12ff00a60349cc5df1e0f45c307c224bf6b88d6c674f8",
                  "fetch_kib": 281189.50, "write_kib": 458783.45, "fetch_scale": 2.0, "write_scale": 1.0}
 # Whole-pass HBM bytes per element (bf16 data, 4-bit code + one 8-bit scale per 16 elements).
 B_AMAX = 2.0

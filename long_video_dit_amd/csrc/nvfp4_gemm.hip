@@ -16,7 +16,8 @@
 //
 // Two kernels share that decode and MFMA code.  Both take a 256 x 256 output
 // tile per 256-thread workgroup (4 waves in 2 x 2, 128 x 128 per wave = 4 x 4
-// MFMA tiles of 32 x 32); within a stage the K order is permuted the same way
+// MFMA tiles of 32 x 32; the fast kernel also 256 x 192, 4 x 3 per wave);
+// within a stage the K order is permuted the same way
 // for A and B: lane half h of k16-step t of sub-chunk s carries
 // k = 64 s + 32 h + 8 t + (0..7), so every lane reads its 32 codes of a
 // sub-chunk with one 16-byte LDS read.
@@ -24,7 +25,8 @@
 //     workgroup per CU walking its tiles; stages of K = 256 copied global ->
 //     LDS by the DMA path (global_load_lds_dwordx4), two stages plus a 16 KB
 //     epilogue buffer in the 160 KB of LDS; hand-interleaved MFMA / decode
-//     steps.
+//     steps; each tile starts with zero-accumulator MFMAs instead of zeroing
+//     its accumulators.
 //   gemm_w4a4_kernel (any K % 16 == 0, any alignment): one tile per
 //     workgroup, register-staged stages of K = 128, double-buffered LDS
 //     (72 KB), zero-filled K tails.
