@@ -108,7 +108,9 @@ def time_calls(torch, fn, steps, warmup):
 
 def time_calls_dist(torch, fn, steps, warmup):
     """Per-call ms of fn() over `steps` calls, an HIP event pair around each
-    call on the current stream: (mean, p10, median, p90)."""
+    call on the current stream: (mean, p10, median, p90).  Each pair adds the
+    call's launch latency, a few us, so the reported means come from
+    time_calls (one pair around back-to-back calls) and these give the spread."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -451,8 +453,10 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         gemm = lambda: nvfp4.gemm(aq, wq, out=cbuf)
         quant()
         settle(torch, gemm)
-        q_ms, *q_pct = time_calls_dist(torch, quant, steps, warmup)
-        g_ms, *g_pct = time_calls_dist(torch, gemm, steps, warmup)
+        q_ms = time_calls(torch, quant, steps, warmup)
+        g_ms = time_calls(torch, gemm, steps, warmup)
+        _, *q_pct = time_calls_dist(torch, quant, steps, 0)
+        _, *g_pct = time_calls_dist(torch, gemm, steps, 0)
         f_ms = time_calls(torch, lambda: nvfp4.gemm_fused_act(a, wq, out=cbuf, a_q=aq), steps, warmup)
         q_ms_g = time_graph(torch, quant)
         g_ms_g = time_graph(torch, gemm, calls=10 if flop_of(M, N, K) > 1e11 else 20)
@@ -503,7 +507,8 @@ def all_configs(torch, nvfp4, workloads, dev, steps, warmup):
         nvfp4.kv_dequantize(*qv, out=ov)
 
     settle(torch, rt)
-    rt_ms, *rt_pct = time_calls_dist(torch, rt, steps, warmup)
+    rt_ms = time_calls(torch, rt, steps, warmup)
+    _, *rt_pct = time_calls_dist(torch, rt, steps, 0)
     n = 2 * k.numel()
     kb = workloads.bf16_bits(k_cpu[:1])
     t0 = time.perf_counter()
